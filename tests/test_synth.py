@@ -1,0 +1,85 @@
+"""The seeded input generators: counter generator against its published
+definition, the C host fill against the NumPy definition, structure of the
+synthetic logits, planted router and draft trees (CPU only)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import fp
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_splitmix64_reference_outputs():
+    with open(os.path.join(GOLDEN, "splitmix64_seed1234567.json")) as f:
+        g = json.load(f)
+    got = synth.splitmix64_sequence(g["seed"], len(g["outputs"]))
+    assert [int(v) for v in got] == [int(v) for v in g["outputs"]]
+
+
+def test_bf16_round_to_nearest_even():
+    one = np.float32(1.0)
+    cases = {1.0: 0x3F80, 1.0 + 2 ** -8: 0x3F80, 1.0 + 3 * 2 ** -8: 0x3F82,
+             1.0 + 2 ** -8 + 2 ** -20: 0x3F81, -2.0: 0xC000, 0.0: 0x0000}
+    for v, bits in cases.items():
+        assert int(synth.f32_to_bf16_rne(np.array([v], np.float32))[0]) == bits, v
+    assert one == 1
+
+
+def test_e4m3fn_encode_roundtrip_and_ties():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = fp.e4m3fn_to_f64(codes).astype(np.float32)
+    back = synth.f32_to_e4m3fn_rne(vals)
+    assert np.array_equal(back, codes)
+    # midpoints between neighbours round to the even code
+    pos = np.array(sorted(set(fp.E4M3FN_TABLE[:0x7F].tolist())))
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = np.float32((a + b) / 2)
+        c = int(synth.f32_to_e4m3fn_rne(np.array([mid]))[0])
+        ca = int(synth.f32_to_e4m3fn_rne(np.array([a], np.float32))[0])
+        cb = int(synth.f32_to_e4m3fn_rne(np.array([b], np.float32))[0])
+        assert c == (ca if ca % 2 == 0 else cb)
+    assert int(synth.f32_to_e4m3fn_rne(np.array([1000.0], np.float32))[0]) == 0x7E
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "scale"])
+def test_host_fill_matches_numpy_definition(kind):
+    n = 50_000 if kind != "scale" else 500
+    out = synth.host_fill(kind, 3, n, seed=0, layer=7, expert0=11, matrix=1)
+    for j in range(3):
+        sid = synth.stream_id(0, 7, 11 + j, 1)
+        ref = {"bf16": synth.counter_bf16, "fp8": synth.counter_fp8,
+               "scale": synth.counter_scales}[kind](sid, 0, n)
+        assert np.array_equal(out[j], ref)
+
+
+def test_weight_statistics():
+    w = synth.host_fill("bf16", 1, 1_000_000, 0, 0, 0, 0)[0]
+    v = fp.bf16_to_f64(w)
+    assert abs(v.std() - 0.02) < 2e-4 and abs(v.mean()) < 1e-4
+    q = fp.e4m3fn_to_f64(synth.host_fill("fp8", 1, 1_000_000, 0, 0, 0, 0)[0])
+    assert abs(q.std() - 64) < 1.0 and np.abs(q).max() <= 224
+
+
+def test_planted_router_reproduces_logits():
+    rng = synth.rng_for(0, 1, 0)
+    x = rng.standard_normal((5, 512)).astype(np.float32)
+    L = synth.structured_logits(rng, 1, 5, 64, 0.05)
+    Wr = synth.planted_router(x, L)
+    assert np.allclose(x.astype(np.float64) @ Wr.astype(np.float64).T, L, atol=1e-4)
+
+
+def test_draft_trees_structure():
+    tr = synth.draft_trees(seed=0, nt=16, n_layers=36, E=128, k=4)
+    assert tr.parent.tolist() == [-1, -1, 0, 0, 1, 1, 2, 2, 3, 3, 4, 4, 5, 5]
+    assert tr.F.shape == (16, 14, 144)
+    for i, p in enumerate(tr.parent):
+        if p >= 0:
+            assert np.all(tr.P[:, i] <= tr.P[:, p])
+            assert np.all((tr.F[:, p] & ~tr.F[:, i]) == 0)     # parent footprint within child's
+    depth = np.array([1, 1, 2, 2, 2, 2, 3, 3, 3, 3, 3, 3, 3, 3])
+    pc = np.unpackbits(tr.F.view(np.uint8), axis=-1).sum(-1)
+    assert np.all(pc <= depth[None] * 36 * 4) and np.all(pc >= 36 * 4)
