@@ -1,0 +1,173 @@
+/*
+ * moe_verify.h -- C ABI of libmoeverify.so, the union-expert MoE verify layer
+ * and cost-aware draft selection for MI355X (gfx950).
+ *
+ * Pages cited:
+ *   [EcoSpec] review of "Less Experts, Faster Decoding: Cost-Aware Speculative
+ *             Decoding for Mixture-of-Experts";
+ *   [S2-MoE]  walkthrough of S^2-MoE (self-speculative decoding for MoE on
+ *             edge devices).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer; the library allocates nothing, keeps no per-call state and never
+ *     synchronises the stream.  Work is enqueued on `stream` (a hipStream_t
+ *     passed as void*; NULL = the null stream); outputs are valid once that
+ *     work completes.  Calls on different streams may run concurrently if
+ *     their output and workspace buffers are disjoint.
+ *   - Arrays are dense, row-major, without padding.
+ *   - Return codes: 0 = OK, MOE_EINVAL (null pointer, shape or range error),
+ *     MOE_ENOTSUP (shape/dtype outside the built kernels), MOE_EWORKSPACE
+ *     (workspace too small), MOE_EHIP (a HIP launch failed).  Arguments are
+ *     validated on the host before anything is enqueued; on a non-zero return
+ *     nothing has been enqueued, except after MOE_EHIP.  moe_last_error()
+ *     gives a message for the calling thread's last non-zero return.
+ *   - Non-finite inputs give undefined (but memory-safe) results.
+ */
+#ifndef MOE_VERIFY_H
+#define MOE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)
+#define MOE_ENOTSUP (-2)
+#define MOE_EWORKSPACE (-3)
+#define MOE_EHIP (-4)
+
+#define MOE_MAX_TOKENS 64
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_TOPK 32
+#define MOE_NUM_STAGES 5   /* router, route, gate-up, down, combine */
+
+/* Expert weight formats.  MOE_FP8_E4M3 is OCP FP8 E4M3FN with one float32
+ * scale per 128 x 128 block (row block, column block), row-major over blocks:
+ * W[i][j] = e4m3fn(q[i][j]) * scale[i / 128][j / 128]. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* One MoE layer.  Routed experts use SwiGLU:
+ *   FFN_e(x) = W_d,e (SiLU(W_g,e x) * (W_u,e x)),  SiLU(z) = z / (1 + e^-z).
+ * W_gu holds, per expert, the I gate rows followed by the I up rows.
+ *   Wr    [E, H]      float32 router
+ *   W_gu  [E, 2I, H]  wdtype (float32 / bf16 bits / fp8 codes)
+ *   W_d   [E, H, I]   wdtype
+ *   s_gu  [E, 2I/128, H/128] float32, s_d [E, H/128, I/128] float32: fp8 only,
+ *         else NULL.
+ *   Wsh_gu [2I, H], Wsh_d [H, I] (+ ssh_gu, ssh_d for fp8): optional always-on
+ *         shared expert, weight 1 for every token, outside the union; NULL if
+ *         absent. */
+typedef struct {
+    int32_t H, I, E, k;
+    int32_t wdtype; /* moe_dtype */
+    const float *Wr;
+    const void *W_gu;
+    const void *W_d;
+    const float *s_gu, *s_d;
+    const void *Wsh_gu, *Wsh_d;
+    const float *ssh_gu, *ssh_d;
+} moe_layer;
+
+/* Optional reuse-aware soft routing bias ([S2-MoE] component 2, steps 1-3,
+ * Fig. 5), applied before the union is formed:
+ *   g_e    = sum_b w_conf[b] * softmax(l_b)_e * [e in TopK(l_b)]
+ *   P*     = the first `cap` experts by (g desc, index asc) with g_e > 0
+ *   lambda_b = alpha * (l_b,(1) - l_b,(k+1))        (float32, no FMA; 0 if k == E)
+ *   l'_b,e = l_b,e + lambda_b for e in P*           (float32)
+ * The selection is the top-k of l'; gate weights are the softmax of the
+ * ORIGINAL logits over that selection.  Requires k <= cap <= E,
+ * 0 <= alpha < 1, w_conf [T] float32 (device) non-negative. */
+typedef struct {
+    int32_t cap;
+    float alpha;
+    const float *w_conf;
+} moe_bias;
+
+/* Optional outputs of moe_verify_layer (device pointers); any field may be
+ * NULL, in which case the value lives only in the workspace.
+ *   logits [T, E] f32          router logits
+ *   topk_idx [T, k] i32        selected experts in rank order (logit desc,
+ *                              index asc; biased logits when bias is on)
+ *   topk_w [T, k] f32          gate weights
+ *   union_size [1] i32         number of unique routed experts U
+ *   union_experts [E] i32      first U entries: the union, ascending
+ *   csr_ptr [E + 1] i32        first U + 1 entries: offsets into csr_tok
+ *   csr_tok [T * k] i32        tokens of each union expert, ascending
+ *   csr_w [T * k] f32          gate weight of each (expert, token) entry
+ *   pstar [E] i32, pstar_size [1] i32   preferred set P* (bias only)
+ *   events: NULL or (host) array of MOE_NUM_STAGES + 1 hipEvent_t handles
+ *           created by the caller; event i is recorded on `stream` before
+ *           stage i and event MOE_NUM_STAGES after the last stage. */
+typedef struct {
+    float *logits;
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *union_size;
+    int32_t *union_experts;
+    int32_t *csr_ptr;
+    int32_t *csr_tok;
+    float *csr_w;
+    int32_t *pstar;
+    int32_t *pstar_size;
+    void *const *events;
+} moe_aux;
+
+/* Workspace bytes that moe_verify_layer needs for this layer, T and bias
+ * (host computation only; bias may be NULL).  Returns 0 for invalid input. */
+size_t moe_verify_workspace_bytes(const moe_layer *layer, int32_t T, const moe_bias *bias);
+
+/* The MoE-layer verify step ([EcoSpec] §1-§2: the verify cost at a layer is
+ * the union of the experts the verified tokens route to; [S2-MoE] motivation,
+ * challenge 2).  For T tokens x [T, H] float32 (device):
+ *   logits = x Wr^T; per-token top-k (+ optional bias); gate weights;
+ *   union U of the selected experts and the token-by-expert grouping;
+ *   y[t] = sum_j w_tj FFN_{e_tj}(x_t) (+ shared expert), y [T, H] float32.
+ * Each unique expert's weights are read once and applied to all of its tokens.
+ * layer (host), bias (host, NULL = off), aux (host, NULL = no extra outputs).
+ * ws: device workspace of at least moe_verify_workspace_bytes() bytes,
+ * 256-byte aligned; its contents need no initialisation and are clobbered.
+ * Limits: 1 <= T <= 64, 1 <= k <= min(E, 32), E <= 512; bf16: H, I multiples
+ * of 32; fp8: H, I multiples of 128.  Numerics: router GEMV and FFN
+ * accumulate in float32; activations enter the bf16/fp8 matrix-core
+ * products as a bf16 high/low pair when T <= 32 (as one bf16 otherwise). */
+int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const moe_bias *bias,
+                     float *y, moe_aux *aux, void *ws, size_t ws_bytes, void *stream);
+
+/* Per-layer union statistics ([S2-MoE] motivation, challenge 2: reuse ratio
+ * = number of distinct experts over s * k).  topk_idx [nL, T, k] int32
+ * (device), entries in [0, E) (entries outside are ignored);
+ * counts [nL] int32 = |union of layer l|, reuse [nL] float32 =
+ * counts / (T * k), correctly rounded.  Limits: 1 <= E <= 65536. */
+int union_stats(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32_t E,
+                int32_t *counts, float *reuse, void *stream);
+
+/* EcoSpec cost-aware greedy draft selection ([EcoSpec] §3.2 global expert
+ * buffer, §3.3 score equation and greedy selection), for nt trees with the
+ * same shape.
+ *   parent (host) [N]: BFS order, parent[i] in [-1, i) (-1 = child of the
+ *                  root); validated, so ties go to ancestors.
+ *   P [nt, N] float32: path probabilities.
+ *   Epred [nt, N, W] uint32: path footprints, bit b = layer * E + expert in
+ *                  word b / 32, LSB first.
+ * For each tree, starting from an empty buffer B, gamma times: score every
+ * unchosen node t as P_t / (popcount(F_t & ~B) + eps) in float32 (add, then
+ * divide, each correctly rounded), choose the highest score (ties: lowest
+ * node index), B |= F_chosen.  S [nt, gamma] int32 receives node ids in
+ * choice order.  P, Epred and S may be NULL when gamma == 0 or nt == 0.
+ * Limits: 0 <= gamma <= N <= 4096, 1 <= W <= 4096, N * W + W + N / 32 <= 16384
+ * (the tree is staged in 64 KB of LDS), eps > 0. */
+int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred,
+                  int32_t W, int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream);
+
+/* Message for the calling thread's last non-zero return ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_VERIFY_H */

@@ -1,0 +1,260 @@
+"""Python binding of libmoeverify (the union-expert MoE verify layer and
+EcoSpec cost-aware draft selection for MI355X).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream.  If the library is
+not built, the first call raises; there is no fallback.
+
+Entry points (same names as the C ABI in include/moe_verify.h):
+  verify_layer(x, layer, bias=None)   -> (y, aux)
+  union_stats(topk_idx, E)            -> (counts, reuse)
+  select_drafts(parent, P, Epred, gamma, eps=1e-6) -> S
+  workspace_bytes(layer, T, bias=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoeverify.so")
+
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+NUM_STAGES = 5
+STAGE_NAMES = ("router", "route", "gate_up", "down", "combine")
+EXPORTED = ("moe_verify_workspace_bytes", "moe_verify_layer", "union_stats", "select_drafts",
+            "moe_last_error")
+
+_vp, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("H", _i32), ("I", _i32), ("E", _i32), ("k", _i32), ("wdtype", _i32),
+                ("Wr", _vp), ("W_gu", _vp), ("W_d", _vp), ("s_gu", _vp), ("s_d", _vp),
+                ("Wsh_gu", _vp), ("Wsh_d", _vp), ("ssh_gu", _vp), ("ssh_d", _vp)]
+
+
+class _Bias(ctypes.Structure):
+    _fields_ = [("cap", _i32), ("alpha", _f32), ("w_conf", _vp)]
+
+
+class _Aux(ctypes.Structure):
+    _fields_ = [("logits", _vp), ("topk_idx", _vp), ("topk_w", _vp), ("union_size", _vp),
+                ("union_experts", _vp), ("csr_ptr", _vp), ("csr_tok", _vp), ("csr_w", _vp),
+                ("pstar", _vp), ("pstar_size", _vp), ("events", _vp)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoeverify.so from this package directory (raises if missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build()); "
+                              "there is no fallback implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_verify_workspace_bytes.argtypes = [ctypes.POINTER(_Layer), _i32, ctypes.POINTER(_Bias)]
+        L.moe_verify_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_verify_layer.argtypes = [ctypes.POINTER(_Layer), _vp, _i32, ctypes.POINTER(_Bias), _vp,
+                                       ctypes.POINTER(_Aux), _vp, ctypes.c_size_t, _vp]
+        L.moe_verify_layer.restype = ctypes.c_int
+        L.union_stats.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+        L.union_stats.restype = ctypes.c_int
+        L.select_drafts.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _vp]
+        L.select_drafts.restype = ctypes.c_int
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libmoeverify error {code}: {msg}")
+        self.code = code
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise MoeError(rc, lib().moe_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+@dataclass
+class LayerWeights:
+    """Device tensors of one MoE layer (layouts in include/moe_verify.h).
+
+    wdtype 'f32' uses float32 W_gu/W_d; 'bf16' uses bf16 or uint16 bit
+    tensors; 'fp8' uses uint8 (or float8_e4m3fn) codes with float32 block
+    scales s_gu [E, 2I/128, H/128] and s_d [E, H/128, I/128]."""
+    H: int
+    I: int
+    E: int
+    k: int
+    wdtype: str
+    Wr: object
+    W_gu: object
+    W_d: object
+    s_gu: object = None
+    s_d: object = None
+    Wsh_gu: object = None
+    Wsh_d: object = None
+    ssh_gu: object = None
+    ssh_d: object = None
+
+    def _c(self) -> _Layer:
+        return _Layer(self.H, self.I, self.E, self.k, DTYPES[self.wdtype], _ptr(self.Wr), _ptr(self.W_gu),
+                      _ptr(self.W_d), _ptr(self.s_gu), _ptr(self.s_d), _ptr(self.Wsh_gu), _ptr(self.Wsh_d),
+                      _ptr(self.ssh_gu), _ptr(self.ssh_d))
+
+
+@dataclass
+class Bias:
+    """Reuse-aware soft bias parameters (w_conf: [T] float32 device tensor)."""
+    cap: int
+    alpha: float
+    w_conf: object
+
+    def _c(self) -> _Bias:
+        return _Bias(self.cap, self.alpha, _ptr(self.w_conf))
+
+
+def workspace_bytes(layer: LayerWeights, T: int, bias: Optional[Bias] = None) -> int:
+    L = layer._c()
+    b = bias._c() if bias is not None else None
+    n = lib().moe_verify_workspace_bytes(ctypes.byref(L), T, ctypes.byref(b) if b else None)
+    if n == 0:
+        raise MoeError(-1, lib().moe_last_error().decode())
+    return int(n)
+
+
+def expert_bytes(H: int, I: int, wdtype: str) -> int:
+    """Bytes of one expert's weights (gate, up and down) plus fp8 block scales."""
+    if wdtype == "f32":
+        return 3 * H * I * 4
+    if wdtype == "bf16":
+        return 3 * H * I * 2
+    if wdtype == "fp8":
+        return 3 * H * I + (2 * I // 128) * (H // 128) * 4 + (H // 128) * (I // 128) * 4
+    raise ValueError(wdtype)
+
+
+@dataclass
+class Aux:
+    logits: object
+    topk_idx: object
+    topk_w: object
+    union_size: object
+    union_experts: object
+    csr_ptr: object
+    csr_tok: object
+    csr_w: object
+    pstar: object
+    pstar_size: object
+
+
+@dataclass
+class Workspace:
+    """Reusable device workspace plus output buffers for one (layer shape, T)."""
+    ws: object
+    nbytes: int
+    aux: Optional[Aux] = None
+    extra: dict = field(default_factory=dict)
+
+
+def alloc_aux(layer: LayerWeights, T: int, device) -> Aux:
+    import torch
+    E, k = layer.E, layer.k
+    i32, f32 = torch.int32, torch.float32
+    return Aux(logits=torch.empty((T, E), dtype=f32, device=device),
+               topk_idx=torch.empty((T, k), dtype=i32, device=device),
+               topk_w=torch.empty((T, k), dtype=f32, device=device),
+               union_size=torch.empty(1, dtype=i32, device=device),
+               union_experts=torch.empty(E, dtype=i32, device=device),
+               csr_ptr=torch.empty(E + 1, dtype=i32, device=device),
+               csr_tok=torch.empty(T * k, dtype=i32, device=device),
+               csr_w=torch.empty(T * k, dtype=f32, device=device),
+               pstar=torch.empty(E, dtype=i32, device=device),
+               pstar_size=torch.empty(1, dtype=i32, device=device))
+
+
+def alloc_workspace(layer: LayerWeights, T: int, bias: Optional[Bias] = None, device=None,
+                    with_aux: bool = True) -> Workspace:
+    import torch
+    device = device or layer.Wr.device
+    n = workspace_bytes(layer, T, bias)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + n]
+    return Workspace(ws=ws, nbytes=n, aux=alloc_aux(layer, T, device) if with_aux else None)
+
+
+def verify_layer(x, layer: LayerWeights, bias: Optional[Bias] = None, *, out=None,
+                 workspace: Optional[Workspace] = None, events: Optional[Sequence] = None, stream=None):
+    """One MoE-layer verify step for x [T, H] float32 (device).  Returns
+    (y [T, H] float32, Aux or None)."""
+    import torch
+    T = int(x.shape[0])
+    if x.dtype != torch.float32 or x.dim() != 2 or x.shape[1] != layer.H or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 [T, H] tensor")
+    if workspace is None:
+        workspace = alloc_workspace(layer, T, bias, device=x.device)
+    y = out if out is not None else torch.empty_like(x)
+    L = layer._c()
+    b = bias._c() if bias is not None else None
+    a = workspace.aux
+    ev_arr = None
+    if events is not None:
+        ev_arr = (ctypes.c_void_p * (NUM_STAGES + 1))(*[int(e.cuda_event) if hasattr(e, "cuda_event") else int(e)
+                                                         for e in events])
+    caux = _Aux(*([_ptr(getattr(a, f)) for f in Aux.__dataclass_fields__] if a else [None] * 10),
+                ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+    rc = lib().moe_verify_layer(ctypes.byref(L), x.data_ptr(), T, ctypes.byref(b) if b else None, y.data_ptr(),
+                                ctypes.byref(caux), workspace.ws.data_ptr(), workspace.nbytes, s)
+    _check(rc)
+    return y, a
+
+
+def union_stats(topk_idx, E: int, counts=None, reuse=None, stream=None):
+    """counts [nL] int32 and reuse [nL] float32 for topk_idx [nL, T, k] int32."""
+    import torch
+    if topk_idx.dtype != torch.int32 or topk_idx.dim() != 3 or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be a contiguous int32 [nL, T, k] tensor")
+    nL, T, k = (int(v) for v in topk_idx.shape)
+    counts = counts if counts is not None else torch.empty(nL, dtype=torch.int32, device=topk_idx.device)
+    reuse = reuse if reuse is not None else torch.empty(nL, dtype=torch.float32, device=topk_idx.device)
+    s = stream if stream is not None else torch.cuda.current_stream(topk_idx.device).cuda_stream
+    _check(lib().union_stats(topk_idx.data_ptr(), nL, T, k, E, counts.data_ptr(), reuse.data_ptr(), s))
+    return counts, reuse
+
+
+def select_drafts(parent, P, Epred, gamma: int, eps: float = 1e-6, out=None, stream=None):
+    """EcoSpec greedy selection for nt trees: parent (host) [N], P [nt, N]
+    float32 and Epred [nt, N, W] uint32/int32 (device).  Returns S [nt, gamma]
+    int32 (device)."""
+    import torch
+    par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+    if P.dtype != torch.float32 or P.dim() != 2 or not P.is_contiguous():
+        raise ValueError("P must be a contiguous float32 [nt, N] tensor")
+    if Epred.dim() != 3 or Epred.element_size() != 4 or not Epred.is_contiguous():
+        raise ValueError("Epred must be a contiguous 32-bit [nt, N, W] tensor")
+    nt, N = (int(v) for v in P.shape)
+    if tuple(Epred.shape[:2]) != (nt, N) or par.shape != (N,):
+        raise ValueError("shape mismatch between parent, P and Epred")
+    W = int(Epred.shape[2])
+    S = out if out is not None else torch.empty((nt, gamma), dtype=torch.int32, device=P.device)
+    s = stream if stream is not None else torch.cuda.current_stream(P.device).cuda_stream
+    _check(lib().select_drafts(par.ctypes.data, N, P.data_ptr(), Epred.data_ptr(), W, gamma, eps, nt,
+                               S.data_ptr(), s))
+    return S

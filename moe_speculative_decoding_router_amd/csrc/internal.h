@@ -1,0 +1,65 @@
+// Internal declarations shared by the HIP translation units of libmoeverify.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Everything one verify-layer call needs, passed by value to every kernel.
+struct VerifyParams {
+    int T, H, I, E, k, wdtype;
+    int cols;        // compact B-operand columns: 2T (high/low split) or T
+    int split;       // 1 if activations enter the products as a bf16 hi/lo pair
+    int has_shared;  // always-on shared expert present
+    int bias_on, cap;
+    int max_slots;   // min(E, T k) + has_shared: bound on the device slot count
+    float alpha;
+
+    const float *x, *Wr;
+    const void *W_gu, *W_d, *Wsh_gu, *Wsh_d;
+    const float *s_gu, *s_d, *ssh_gu, *ssh_d;
+    const float *w_conf;
+    float *y;
+
+    // routing outputs (caller buffers or workspace)
+    float *logits;
+    int *topk_idx;
+    float *topk_w;
+    int *union_experts, *csr_ptr, *csr_tok;
+    float *csr_w;
+    int *pstar;
+    int *union_size_out, *pstar_size_out;  // may be null
+
+    // workspace-only tables
+    int *meta;         // [0] union size U, [1] slots (U + shared), [2] |P*|
+    int *slot_expert;  // [slots] expert id per slot (E = shared expert)
+    float *tokw;       // [slots * T] gate weight of token t in slot s (0 if not routed)
+    int *tokpos;       // [slots * T] row of ydown for (slot, token), -1 if not routed
+    int *tpos;         // [T * k] row of ydown for (token, rank)
+    uint16_t *xB;      // [H * cols] bf16 activations in the matrix-core operand order
+    uint16_t *hB;      // [max_slots * I * cols] bf16 hidden activations, weighted
+    float *h32;        // [max_slots * T * I] float32 hidden (float32 weights)
+    float *ydown;      // [(T * k + T) * H] per-(token, expert) outputs
+};
+
+constexpr int kWaveSize = 64;
+
+// Launchers (enqueue only; return hipError_t of the launch).
+hipError_t launch_router(const VerifyParams &p, hipStream_t s);
+hipError_t launch_route(const VerifyParams &p, hipStream_t s);
+hipError_t launch_gateup(const VerifyParams &p, int n_cu, hipStream_t s);
+hipError_t launch_down(const VerifyParams &p, int n_cu, hipStream_t s);
+hipError_t launch_combine(const VerifyParams &p, hipStream_t s);
+hipError_t launch_union_stats(const int32_t *topk_idx, int nL, int T, int k, int E, int32_t *counts,
+                              float *reuse, hipStream_t s);
+hipError_t launch_select(int N, const float *P, const uint32_t *F, int W, int gamma, float eps,
+                         int nt, int32_t *S, hipStream_t s);
+
+// Limits used by the kernels.
+constexpr int kMaxTokens = 64;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 32;
+constexpr int kSelectMaxLdsWords = 16384;  // 64 KB of footprint words per tree
+
+}  // namespace moe

@@ -40,6 +40,7 @@ import ctypes
 import math
 import os
 from dataclasses import dataclass
+from typing import Optional
 
 import numpy as np
 
@@ -353,3 +354,103 @@ def pack_bits(bits: np.ndarray, W: int) -> np.ndarray:
     b = b.reshape(bits.shape[:-1] + (W, 32)).astype(np.uint64)
     weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
     return (b * weights).sum(axis=-1).astype(np.uint32)
+
+
+# ----------------------------------------------------------------------------
+# Workloads: the verify-layer configurations, their inputs and weights
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Workload:
+    """One verify-layer configuration (shapes, weight format, routing skew)."""
+    name: str
+    H: int
+    I: int
+    E: int
+    k: int
+    T: int
+    wdtype: str              # 'f32' | 'bf16' | 'fp8'
+    rate: float = 0.05       # popularity decay rate of the logit generator
+    n_seq: int = 1           # sequences sharing the T tokens (T // n_seq each)
+    shared: bool = False     # one always-on shared expert
+    n_layers: int = 1
+    seed: int = 0
+    cid: int = 0             # configuration id used in the seed path
+
+
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", H=256, I=512, E=8, k=2, T=5, wdtype="f32", cid=0),
+    "qwen3_bf16": Workload("qwen3_bf16", H=4096, I=1536, E=128, k=8, T=5, wdtype="bf16", rate=0.05, cid=1),
+    "gptoss_bf16": Workload("gptoss_bf16", H=2880, I=2880, E=128, k=4, T=5, wdtype="bf16", rate=0.05, cid=2),
+    "deepseek_fp8": Workload("deepseek_fp8", H=7168, I=2048, E=256, k=8, T=5, wdtype="fp8", rate=0.01,
+                             shared=True, n_layers=16, cid=3),
+    "qwen3_batch4_bf16": Workload("qwen3_batch4_bf16", H=4096, I=1536, E=128, k=8, T=20, wdtype="bf16",
+                                  rate=0.05, n_seq=4, n_layers=40, cid=4),
+}
+
+
+def tiny_f32_arrays(wl: Workload):
+    """Tiny float32 layer drawn with NumPy (seed wl.seed) in the order x, Wr,
+    gate, up, down; weights ~N(0, 0.02), x ~N(0, 1).  W_gu = [gate; up]."""
+    rng = np.random.default_rng(wl.seed)
+    x = rng.standard_normal((wl.T, wl.H)).astype(np.float32)
+    Wr = (0.02 * rng.standard_normal((wl.E, wl.H))).astype(np.float32)
+    gate = (0.02 * rng.standard_normal((wl.E, wl.I, wl.H))).astype(np.float32)
+    up = (0.02 * rng.standard_normal((wl.E, wl.I, wl.H))).astype(np.float32)
+    down = (0.02 * rng.standard_normal((wl.E, wl.H, wl.I))).astype(np.float32)
+    return x, Wr, np.concatenate([gate, up], axis=1), down
+
+
+def layer_inputs(wl: Workload, layer: int, T: Optional[int] = None, n_seq: Optional[int] = None):
+    """x [T, H] float32, target logits [T, E] float64 and planted router
+    Wr [E, H] float32 for one layer (structured logits, planted router)."""
+    T = wl.T if T is None else T
+    n_seq = wl.n_seq if n_seq is None else n_seq
+    rng = rng_for(wl.seed, wl.cid, layer, T, n_seq)
+    x = rng.standard_normal((T, wl.H)).astype(np.float32)
+    L = structured_logits(rng, n_seq, T // n_seq, wl.E, wl.rate)
+    return x, L, planted_router(x, L)
+
+
+def fill_layer_device(wl: Workload, layer: int, device, stream: int = 0) -> dict:
+    """Expert weights of one layer written on the device by the counter fill.
+    Returns torch tensors W_gu, W_d (+ s_gu, s_d, shared expert)."""
+    import torch
+    E, H, I = wl.E, wl.H, wl.I
+    out = {}
+    if wl.wdtype == "bf16":
+        out["W_gu"] = torch.empty((E, 2 * I, H), dtype=torch.int16, device=device)
+        out["W_d"] = torch.empty((E, H, I), dtype=torch.int16, device=device)
+        dev_fill("bf16", out["W_gu"].data_ptr(), E, 2 * I * H, wl.seed, layer, 0, MAT_GU, stream)
+        dev_fill("bf16", out["W_d"].data_ptr(), E, H * I, wl.seed, layer, 0, MAT_D, stream)
+    elif wl.wdtype == "fp8":
+        nE = E + (1 if wl.shared else 0)
+        gu = torch.empty((nE, 2 * I, H), dtype=torch.uint8, device=device)
+        d = torch.empty((nE, H, I), dtype=torch.uint8, device=device)
+        sgu = torch.empty((nE, 2 * I // 128, H // 128), dtype=torch.float32, device=device)
+        sd = torch.empty((nE, H // 128, I // 128), dtype=torch.float32, device=device)
+        dev_fill("fp8", gu.data_ptr(), nE, 2 * I * H, wl.seed, layer, 0, MAT_GU, stream)
+        dev_fill("fp8", d.data_ptr(), nE, H * I, wl.seed, layer, 0, MAT_D, stream)
+        dev_fill("scale", sgu.data_ptr(), nE, sgu[0].numel(), wl.seed, layer, 0, MAT_GU_SCALE, stream)
+        dev_fill("scale", sd.data_ptr(), nE, sd[0].numel(), wl.seed, layer, 0, MAT_D_SCALE, stream)
+        out.update(W_gu=gu[:E], W_d=d[:E], s_gu=sgu[:E], s_d=sd[:E])
+        if wl.shared:
+            out.update(Wsh_gu=gu[E], Wsh_d=d[E], ssh_gu=sgu[E], ssh_d=sd[E])
+    else:
+        raise ValueError("device fill covers bf16 and fp8 layers")
+    return out
+
+
+def host_expert_raw(wl: Workload, layer: int, expert: int) -> dict:
+    """Raw weight codes of one expert regenerated on the host (expert == E is
+    the shared expert): 'gu' [2I, H], 'd' [H, I] (bf16 bits or fp8 codes) and
+    for fp8 the block scales 's_gu', 's_d'."""
+    H, I = wl.H, wl.I
+    kind = "bf16" if wl.wdtype == "bf16" else "fp8"
+    out = {"gu": host_fill(kind, 1, 2 * I * H, wl.seed, layer, expert, MAT_GU)[0].reshape(2 * I, H),
+           "d": host_fill(kind, 1, H * I, wl.seed, layer, expert, MAT_D)[0].reshape(H, I)}
+    if wl.wdtype == "fp8":
+        out["s_gu"] = host_fill("scale", 1, (2 * I // 128) * (H // 128), wl.seed, layer, expert,
+                                MAT_GU_SCALE)[0].reshape(2 * I // 128, H // 128)
+        out["s_d"] = host_fill("scale", 1, (H // 128) * (I // 128), wl.seed, layer, expert,
+                               MAT_D_SCALE)[0].reshape(H // 128, I // 128)
+    return out

@@ -1,0 +1,110 @@
+"""The C ABI library loads and exports every symbol include/moe_verify.h
+declares; host-side argument validation returns the documented codes before
+anything reaches the GPU (CPU only, no compute calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import moe_speculative_decoding_router_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_verify.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m.LIB_PATH):
+        pytest.fail("libmoeverify.so is not built; run __graft_entry__.build()")
+    return m.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(m.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def layer(**kw):
+    base = dict(H=512, I=256, E=32, k=4, wdtype=m.MOE_BF16, Wr=16, W_gu=16, W_d=16)
+    base.update(kw)
+    L = m._Layer()
+    for k, v in base.items():
+        setattr(L, k, v)
+    return L
+
+
+def ws_bytes(lib, L, T, bias=None):
+    return lib.moe_verify_workspace_bytes(ctypes.byref(L), T, ctypes.byref(bias) if bias else None)
+
+
+def test_workspace_bytes_and_shape_validation(lib):
+    assert ws_bytes(lib, layer(), 5) > 0
+    assert ws_bytes(lib, layer(), 64) > ws_bytes(lib, layer(), 5)
+    for bad in (dict(k=0), dict(k=33, E=64), dict(k=40, E=32), dict(E=513), dict(H=0), dict(wdtype=7),
+                dict(H=500), dict(I=250), dict(wdtype=m.MOE_FP8_E4M3, H=512, I=192)):
+        assert ws_bytes(lib, layer(**bad), 5) == 0, bad
+    assert ws_bytes(lib, layer(), 0) == 0 and ws_bytes(lib, layer(), 65) == 0
+    b = m._Bias(3, 0.5, 16)                       # cap < k
+    assert ws_bytes(lib, layer(), 5, b) == 0 and b"cap" in lib.moe_last_error()
+    b = m._Bias(8, 1.0, 16)                       # alpha outside [0, 1)
+    assert ws_bytes(lib, layer(), 5, b) == 0 and b"alpha" in lib.moe_last_error()
+    assert ws_bytes(lib, layer(), 5, m._Bias(8, 0.5, 16)) > 0
+
+
+def test_verify_layer_rejects_before_launch(lib):
+    L = layer()
+    aux = m._Aux()
+    rc = lib.moe_verify_layer(ctypes.byref(L), None, 5, None, 16, ctypes.byref(aux), 256, 1 << 30, None)
+    assert rc == -1 and b"x and y" in lib.moe_last_error()
+    need = ws_bytes(lib, L, 5)
+    rc = lib.moe_verify_layer(ctypes.byref(L), 16, 5, None, 16, ctypes.byref(aux), 256, need - 1, None)
+    assert rc == -3 and b"workspace" in lib.moe_last_error()
+    rc = lib.moe_verify_layer(ctypes.byref(L), 16, 5, None, 16, ctypes.byref(aux), 255, need, None)
+    assert rc == -1 and b"aligned" in lib.moe_last_error()
+    Lf = layer(wdtype=m.MOE_FP8_E4M3, s_gu=None, s_d=None)
+    rc = lib.moe_verify_layer(ctypes.byref(Lf), 16, 5, None, 16, ctypes.byref(aux), 256, 1 << 30, None)
+    assert rc == -1 and b"s_gu" in lib.moe_last_error()
+    Lx = layer(Wsh_gu=16)
+    rc = lib.moe_verify_layer(ctypes.byref(Lx), 16, 5, None, 16, ctypes.byref(aux), 256, 1 << 30, None)
+    assert rc == -1 and b"shared" in lib.moe_last_error()
+    rc = lib.moe_verify_layer(ctypes.byref(layer(H=4004)), 16, 5, None, 16, ctypes.byref(aux), 256, 1 << 30, None)
+    assert rc == -2
+
+
+def test_union_stats_and_select_validation(lib):
+    assert lib.union_stats(None, 1, 5, 8, 128, 16, 16, None) == -1
+    assert lib.union_stats(16, 1, 0, 8, 128, 16, 16, None) == -1
+    assert lib.union_stats(16, 1, 5, 8, 70000, 16, 16, None) == -1
+    assert lib.union_stats(16, 0, 5, 8, 128, 16, 16, None) == 0          # nothing to do
+    par = np.array([-1, -1, 0, 0, 1, 1], dtype=np.int32)
+    bad = np.array([-1, 2, 0, 0, 1, 1], dtype=np.int32)                   # parent after child
+    assert lib.select_drafts(bad.ctypes.data, 6, 16, 16, 4, 4, 1e-6, 1, 16, None) == -1
+    assert b"BFS" in lib.moe_last_error()
+    assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4, 7, 1e-6, 1, 16, None) == -1   # gamma > N
+    assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4, 4, 0.0, 1, 16, None) == -1    # eps <= 0
+    assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4000, 4, 1e-6, 1, 16, None) == -2  # LDS stage
+    assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4, 0, 1e-6, 1, 16, None) == 0    # gamma 0
+    assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4, 4, 1e-6, 0, 16, None) == 0    # no trees
+
+
+def test_expert_bytes_matches_page_figures():
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "page_figures.json")) as f:
+        g = json.load(f)
+    ds = g["deepseek_fp8_expert"]
+    b = m.expert_bytes(ds["H"], ds["I"], "fp8")
+    assert abs(b / 1e6 - ds["approx_MB"]) < 0.5          # "44 MB" per DeepSeek FP8 expert
+    q = g["table2_qwen_delta"]
+    delta_gb = q["experts_delta"] * q["n_layers"] * m.expert_bytes(q["H"], q["I"], "bf16") / 1e9
+    assert abs(delta_gb - q["page_delta_GB"]) / q["page_delta_GB"] < q["rel_tol"]

@@ -1,0 +1,87 @@
+"""GPU parity of select_drafts and union_stats (bit for bit against the
+oracle) and of the device weight fill against the host generator."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import moe as omoe
+from oracle import select as osel
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import moe_speculative_decoding_router_amd as m  # noqa: E402
+from gpu_helpers import log, to_dev  # noqa: E402
+
+
+def run_select(trees, gamma, eps=1e-6):
+    S = m.select_drafts(trees.parent, to_dev(trees.P), to_dev(trees.F.view(np.int32)), gamma, eps)
+    torch.cuda.synchronize()
+    return S.cpu().numpy()
+
+
+@pytest.mark.parametrize("gamma", [0, 1, 4, 14])
+def test_select_gptoss_trees(gamma):
+    log(f"case select_drafts gptoss trees nt=128 gamma={gamma}")
+    trees = synth.draft_trees(seed=0, nt=128, n_layers=36, E=128, k=4)
+    S = run_select(trees, gamma)
+    ref = osel.select_drafts_batch(trees.P, trees.F, gamma)
+    assert np.array_equal(S, ref)
+
+
+def test_select_ties_and_odd_widths():
+    log("case select_drafts ties / odd W")
+    trees = synth.draft_trees(seed=1, nt=64, n_layers=5, E=37, k=3)   # W = 6 words
+    trees.P[:] = np.float32(0.5)
+    S = run_select(trees, 5)
+    assert np.array_equal(S, osel.select_drafts_batch(trees.P, trees.F, 5))
+    trees.F[:] = trees.F[:, :1]                                          # all footprints equal
+    trees.P[:] = np.random.default_rng(3).uniform(0.1, 1, trees.P.shape).astype(np.float32)
+    S = run_select(trees, 7)
+    assert np.array_equal(S, osel.select_drafts_batch(trees.P, trees.F, 7))
+
+
+def test_select_large_batch_sampled():
+    log("case select_drafts nt=4096 (sampled check)")
+    trees = synth.draft_trees(seed=2, nt=4096, n_layers=36, E=128, k=4)
+    S = run_select(trees, 4)
+    idx = np.random.default_rng(0).choice(4096, 256, replace=False)
+    ref = osel.select_drafts_batch(trees.P[idx], trees.F[idx], 4)
+    assert np.array_equal(S[idx], ref)
+    # every selection is prefix-closed on the tree
+    for row in S:
+        seen = set()
+        for t in row:
+            p = trees.parent[t]
+            assert p < 0 or p in seen
+            seen.add(int(t))
+
+
+@pytest.mark.parametrize("E,T,k", [(128, 5, 8), (128, 20, 8), (300, 7, 3), (8, 4, 2)])
+def test_union_stats(E, T, k):
+    log(f"case union_stats E={E} T={T} k={k}")
+    rng = np.random.default_rng(E + T)
+    nL = 40
+    L = np.stack([synth.structured_logits(rng, 1, T, E, 0.05) for _ in range(nL)]).astype(np.float32)
+    idx = np.stack([omoe.topk(L[l], k) for l in range(nL)])
+    idx[0] = idx[0][:1]                          # identical tokens: union == k
+    counts, reuse = m.union_stats(to_dev(idx), E)
+    torch.cuda.synchronize()
+    rc, rr = omoe.union_stats(idx)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(reuse.cpu().numpy(), rr)
+    assert counts[0].item() == k
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "scale"])
+def test_device_fill_matches_host_generator(kind):
+    n_exp, per = 3, 100_003 if kind != "scale" else 997
+    dt = {"bf16": torch.int16, "fp8": torch.uint8, "scale": torch.float32}[kind]
+    buf = torch.empty((n_exp, per), dtype=dt, device="cuda:0")
+    synth.dev_fill(kind, buf.data_ptr(), n_exp, per, seed=0, layer=5, expert0=9, matrix=1)
+    torch.cuda.synchronize()
+    host = synth.host_fill(kind, n_exp, per, seed=0, layer=5, expert0=9, matrix=1)
+    assert np.array_equal(buf.cpu().numpy().view(host.dtype), host)
