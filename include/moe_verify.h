@@ -52,15 +52,18 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
 /* One MoE layer.  Routed experts use SwiGLU:
  *   FFN_e(x) = W_d,e (SiLU(W_g,e x) * (W_u,e x)),  SiLU(z) = z / (1 + e^-z).
- * W_gu holds, per expert, the I gate rows followed by the I up rows.
- *   Wr    [E, H]      float32 router
- *   W_gu  [E, 2I, H]  wdtype (float32 / bf16 bits / fp8 codes)
- *   W_d   [E, H, I]   wdtype
- *   s_gu  [E, 2I/128, H/128] float32, s_d [E, H/128, I/128] float32: fp8 only,
- *         else NULL.
- *   Wsh_gu [2I, H], Wsh_d [H, I] (+ ssh_gu, ssh_d for fp8): optional always-on
- *         shared expert, weight 1 for every token, outside the union; NULL if
- *         absent. */
+ * Logical shapes: the gate-up matrix [2I, H] holds the I gate rows followed by
+ * the I up rows; the down matrix is [H, I].
+ *   Wr    [E, H]      float32 router, row-major
+ *   W_gu  [E, 2I, H]  float32: row-major.  bf16 / fp8: PACKED by
+ *                     moe_pack_weights(gate_up = 1), same byte size.
+ *   W_d   [E, H, I]   float32: row-major.  bf16 / fp8: PACKED by
+ *                     moe_pack_weights(gate_up = 0).
+ *   s_gu  [E, 2I/128, H/128] float32, s_d [E, H/128, I/128] float32: fp8 block
+ *         scales of the LOGICAL matrices, row-major; NULL otherwise.
+ *   Wsh_gu, Wsh_d (+ ssh_gu, ssh_d for fp8): optional always-on shared expert
+ *         in the same formats with E = 1, weight 1 for every token, outside the
+ *         union; NULL if absent. */
 typedef struct {
     int32_t H, I, E, k;
     int32_t wdtype; /* moe_dtype */
@@ -116,6 +119,22 @@ typedef struct {
     void *const *events;
 } moe_aux;
 
+/* Packs row-major expert weights into the matrix-core tile layout that
+ * moe_verify_layer streams (bf16 or fp8; one-time weight preparation).
+ * src [E, rows, K] row-major (device), dst (device, same byte size, must not
+ * overlap src).  gate_up = 1: src is the gate-up matrix, rows = 2I, K = H;
+ * gate_up = 0: the down matrix, rows = H, K = I.
+ * Layout of dst: per expert, 1 KB tiles of 16 rows x 32 k (bf16) or 16 rows x
+ * 64 k (fp8), row-tile major then K-tile; inside a tile, 16-byte slot
+ * l = 0..63 holds tile row l % 16 at k offset (l / 16) * 8 (bf16) or
+ * (l / 16) * 16 (fp8), the operand order of v_mfma_f32_16x16x32_bf16, so a
+ * wave reads 1 KB of contiguous memory per load.  For gate_up = 1, row tile rt
+ * holds gate rows 8 rt .. 8 rt + 7 as tile rows 0..7 and up rows
+ * I + 8 rt .. I + 8 rt + 7 as tile rows 8..15.
+ * Requires rows % 16 == 0 and K % 32 (bf16) / K % 64 (fp8) == 0. */
+int moe_pack_weights(const void *src, void *dst, int32_t E, int32_t rows, int32_t K, int32_t wdtype,
+                     int32_t gate_up, void *stream);
+
 /* Workspace bytes that moe_verify_layer needs for this layer, T and bias
  * (host computation only; bias may be NULL).  Returns 0 for invalid input. */
 size_t moe_verify_workspace_bytes(const moe_layer *layer, int32_t T, const moe_bias *bias);
@@ -158,7 +177,7 @@ int union_stats(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32
  * divide, each correctly rounded), choose the highest score (ties: lowest
  * node index), B |= F_chosen.  S [nt, gamma] int32 receives node ids in
  * choice order.  P, Epred and S may be NULL when gamma == 0 or nt == 0.
- * Limits: 0 <= gamma <= N <= 4096, 1 <= W <= 4096, N * W + W + N / 32 <= 16384
+ * Limits: 0 <= gamma <= N <= 4096, 1 <= W <= 4096, N * W + W + N + N / 32 <= 16384
  * (the tree is staged in 64 KB of LDS), eps > 0. */
 int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred,
                   int32_t W, int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream);

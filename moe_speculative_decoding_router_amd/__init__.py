@@ -6,6 +6,7 @@ PyTorch provides device memory and the current stream.  If the library is
 not built, the first call raises; there is no fallback.
 
 Entry points (same names as the C ABI in include/moe_verify.h):
+  pack_weights(src, wdtype, gate_up)  -> packed weights (one-time preparation)
   verify_layer(x, layer, bias=None)   -> (y, aux)
   union_stats(topk_idx, E)            -> (counts, reuse)
   select_drafts(parent, P, Epred, gamma, eps=1e-6) -> S
@@ -27,8 +28,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 NUM_STAGES = 5
 STAGE_NAMES = ("router", "route", "gate_up", "down", "combine")
-EXPORTED = ("moe_verify_workspace_bytes", "moe_verify_layer", "union_stats", "select_drafts",
-            "moe_last_error")
+EXPORTED = ("moe_pack_weights", "moe_verify_workspace_bytes", "moe_verify_layer", "union_stats",
+            "select_drafts", "moe_last_error")
 
 _vp, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.union_stats.restype = ctypes.c_int
         L.select_drafts.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _vp]
         L.select_drafts.restype = ctypes.c_int
+        L.moe_pack_weights.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
+        L.moe_pack_weights.restype = ctypes.c_int
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -127,6 +130,33 @@ class Bias:
 
     def _c(self) -> _Bias:
         return _Bias(self.cap, self.alpha, _ptr(self.w_conf))
+
+
+def pack_weights(src, wdtype: str, gate_up: bool, out=None, stream=None):
+    """Pack row-major expert weights src [E, rows, K] (bf16 bits or fp8 codes,
+    device) into the tile layout moe_verify_layer streams.  Returns the packed
+    tensor (same shape and dtype; only the byte order differs)."""
+    import torch
+    if src.dim() == 2:
+        src = src.unsqueeze(0)
+    if src.dim() != 3 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous [E, rows, K] tensor")
+    E, rows, K = (int(v) for v in src.shape)
+    dst = out if out is not None else torch.empty_like(src)
+    s = stream if stream is not None else torch.cuda.current_stream(src.device).cuda_stream
+    _check(lib().moe_pack_weights(src.data_ptr(), dst.data_ptr(), E, rows, K, DTYPES[wdtype], int(bool(gate_up)), s))
+    return dst
+
+
+def pack_layer_tensors(W: dict, wdtype: str) -> dict:
+    """Pack the row-major weight tensors of a layer dict (keys W_gu, W_d and
+    optionally Wsh_gu, Wsh_d); scales and other entries pass through."""
+    out = dict(W)
+    for key, gu in (("W_gu", True), ("W_d", False), ("Wsh_gu", True), ("Wsh_d", False)):
+        if W.get(key) is not None:
+            packed = pack_weights(W[key].contiguous(), wdtype, gu)
+            out[key] = packed if W[key].dim() == 3 else packed[0]
+    return out
 
 
 def workspace_bytes(layer: LayerWeights, T: int, bias: Optional[Bias] = None) -> int:

@@ -16,20 +16,34 @@
 //             small L2-resident buffer.  Partial sums meet in LDS in a fixed
 //             order; SiLU(gate) * up, times the token's gate weight, is
 //             written in the B-operand layout of the down projection.
-//   down    : item = (slot s, 16 output rows), one wave per item over the
-//             full I contraction; per-(token, expert) rows of ydown.
-//   combine : y[t] = sum over the token's k ranks of ydown (+ shared expert),
-//             in rank order, so the output is reproducible.
-// Float32 weights use plain VALU dot products (one wave per output row).
+//   down    : one workgroup per 16 output rows; its waves split the I
+//             contraction and stream that row tile of every union slot, so y
+//             is accumulated in registers over all experts and written once
+//             (deterministic, no atomics, equal bytes per workgroup).
+// Float32 weights use plain VALU dot products (one wave per output row),
+// per-(token, expert) rows of ydown and a combine in rank order.
 #include <math.h>
 
 #include "common.h"
 #include "internal.h"
+#include "route_block.h"
 
 namespace moe {
 namespace {
 
 constexpr int kFfnThreads = 256;
+constexpr int kGateUpWgPerCu = 1;  // persistent workgroups per CU (8 waves each)
+constexpr int kDownWgPerCu = 2;  // capacity bound; the grid is one workgroup per row tile
+constexpr size_t kLdsPerCu = 160 * 1024;      // LDS of one gfx950 compute unit
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l of the wave writes lds_wave_base + 16 l;
+// the base must be the same in every lane.  Completion is tracked by the
+// vector memory counter, so wait_vm_all() and a barrier precede any read.
+__device__ __forceinline__ void load_lds16(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ u32x4 ld_nt(const uint8_t *ptr) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ptr));
@@ -66,261 +80,419 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
-// WT: 0 = bf16, 1 = fp8.  NT: 16-column tiles of the B operand.  SPLIT: the
-// B columns are (hi of token t, lo of token t) pairs.  NKS: waves splitting
-// the contraction of one item.  GU: gate-up (true) or down (false).
-template <int WT, int NT, bool SPLIT, int NKS, bool GU>
-__global__ __launch_bounds__(kFfnThreads) void ffn_mfma_kernel(VerifyParams p) {
-    constexpr int IPW = 4 / NKS;
-    constexpr int NACC = GU ? 2 : 1;
-    constexpr int KU = NT == 1 ? 8 : (NT == 2 ? 4 : 2);  // bf16 k-steps per batch
-    constexpr int KUB = NT == 1 ? 2 : 1;                  // fp8 128-blocks per batch
-    constexpr size_t ESZ = WT == 1 ? 1 : 2;
-    __shared__ f32x4 red[NKS > 1 ? 4 : 1][NACC * NT][64];
+// ---------------------------------------------------------------------------
+// Unit streams.  A unit is one packed tile (bf16: 16 rows x 32 k, one k-step)
+// or one 128-wide scale block (fp8: two tiles, four k-steps).  A wave streams
+// its units in batches of KU with two register buffers: the loads of batch
+// f + 1 are in flight while batch f is multiplied.  Every load is issued
+// unconditionally (out-of-range units re-read a valid tile and are skipped
+// by a wave-uniform test; B columns past the used ones read the padded,
+// never-used part of the operand, which only feeds output columns that are
+// discarded), so the loads of a batch form one straight-line group and the
+// waits before the products count only older loads.
+// ---------------------------------------------------------------------------
+template <int WT, int NT, int KU>
+struct Batch {
+    static constexpr int NA = WT == 1 ? 2 : 1;  // tile loads per unit
+    static constexpr int NS = WT == 1 ? 4 : 1;  // k-steps per unit
+    u32x4 a[KU][NA];
+    u32x4 b[KU][NS][NT];
+    float sc[KU];
+    bool on[KU];
+};
 
+template <int WT, int NT, int KU>
+__device__ __forceinline__ void load_unit(Batch<WT, NT, KU> &bt, int u, bool on, const uint8_t *tile,
+                                          const uint16_t *bq, size_t bstep, float scale, const int (&coff)[NT]) {
+    bt.on[u] = on;
+#pragma unroll
+    for (int h = 0; h < Batch<WT, NT, KU>::NA; ++h) bt.a[u][h] = ld_nt(tile + h * 1024);
+#pragma unroll
+    for (int q = 0; q < Batch<WT, NT, KU>::NS; ++q)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) bt.b[u][q][n] = *reinterpret_cast<const u32x4 *>(bq + q * bstep + coff[n]);
+    bt.sc[u] = scale;
+}
+
+// Element offsets of this lane's B-operand columns (column n * 16 + lr,
+// clamped to the last used column: the clamped lanes re-read a column that
+// the wave loads anyway and only feed output columns that are discarded).
+template <int NT>
+__device__ __forceinline__ void col_offsets(int (&coff)[NT], int lr, int cols) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) coff[n] = min(n * 16 + lr, cols - 1) * 8;
+}
+
+// Products of one batch.  Consecutive units alternate between two
+// accumulator sets so that neighbouring matrix-core instructions are
+// independent; the sets are added at the end of an item.
+template <int WT, int NT, int KU>
+__device__ __forceinline__ void compute_batch(const Batch<WT, NT, KU> &bt, f32x4 (&acc)[2][NT], bool valid) {
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+        // skipped units multiply zeros (no branch, so the waits before the
+        // products only count loads issued before this batch's own)
+        const bool on = valid && bt.on[u];
+        f32x4 (&ac)[NT] = acc[u & 1];
+        if (WT == 0) {
+            const bf16x8 a = as_bf16x8(on ? bt.a[u][0] : zero);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) ac[n] = mfma(a, as_bf16x8(bt.b[u][0][n]), ac[n]);
+        } else {
+            f32x4 t[2][NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) t[0][n] = t[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x8 lo, hi;
+                fp8x16_to_bf16(bt.a[u][h], lo, hi);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    t[0][n] = mfma(lo, as_bf16x8(bt.b[u][2 * h][n]), t[0][n]);
+                    t[1][n] = mfma(hi, as_bf16x8(bt.b[u][2 * h + 1][n]), t[1][n]);
+                }
+            }
+            const float sc = on ? bt.sc[u] : 0.f;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) ac[n] += sc * (t[0][n] + t[1][n]);
+        }
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void fold_acc(f32x4 (&acc)[2][NT]) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        acc[0][n] += acc[1][n];
+        acc[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// Adds the low-part columns to the high-part columns: column c of tile n is
+// token n * 16 + lr; in split mode the low part of token t sits in column
+// T + t (tile (T + t) / 16, lane (T + t) % 16 of the same lane group).
+template <int NT, bool SPLIT>
+__device__ __forceinline__ void combine_split(float (&v)[NT][4], const f32x4 (&acc)[NT], int T, int lane) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[n][j] = acc[n][j];
+    if (!SPLIT) return;
+    const int lr = lane & 15;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const int clo = T + n * 16 + lr;
+        const int nlo = clo >> 4;
+        const int src = (lane & ~15) | (clo & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float lo = 0.f;
+#pragma unroll
+            for (int q = 0; q < NT; ++q) {
+                const float a = __shfl(acc[q][j], src);
+                if (q == nlo) lo = a;
+            }
+            v[n][j] += lo;
+        }
+    }
+}
+
+template <int NT, int NW>
+__device__ __forceinline__ void reduce_waves(f32x4 (&acc)[NT], f32x4 (*red)[NT][64], int w, int lane) {
+    if (w != 0) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) red[w][n][lane] = acc[n];
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+        for (int q = 1; q < NW; ++q)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[n] += red[q][n][lane];
+    }
+}
+
+template <int WT, int NT>
+struct UnitCfg {
+    static constexpr int KT = WT == 1 ? 64 : 32;                                    // k per tile
+    static constexpr int KU = WT == 1 ? (NT == 1 ? 2 : 1)                           // units per batch
+                                      : (NT == 1 ? 8 : (NT == 2 ? 4 : 2));
+    static constexpr size_t USTEP = WT == 1 ? 2048 : 1024;                          // bytes per unit
+    static constexpr int KSTEPS = WT == 1 ? 4 : 1;                                  // k-steps per unit
+};
+
+// ---------------------------------------------------------------------------
+// gate-up: items = (slot, row tile of 8 gate + 8 up rows); a workgroup of 8
+// waves takes items round-robin, its waves take interleaved batches of the
+// H contraction, and the partial sums meet in LDS in a fixed order.  The
+// batches of a wave run across item boundaries, so the next item's weights
+// are in flight while the current item is reduced.
+// BLDS: the activation operand (identical for every item) is copied into
+// LDS once per workgroup, so the only vector-memory traffic of the stream is
+// the weights.  TWL: token weights staged in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kGuWaves = 8;
+
+template <int WT, int NT, bool SPLIT, bool FUSED, bool BLDS>
+__global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
+    using C = UnitCfg<WT, NT>;
+    constexpr int KU = C::KU;
+    using B = Batch<WT, NT, KU>;
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    __shared__ f32x4 red[2][kGuWaves][NT][64];
+    __shared__ int sexp[kMaxExperts + 1];
+    __shared__ int nslots_sh;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int sub = w / NKS, kpart = w % NKS;
-    const int lr = lane & 15, g = lane >> 4;
-    const int T = p.T, H = p.H, I = p.I, E = p.E, cols = p.cols;
-    const int K = GU ? H : I;
-    const int tiles = (GU ? I : H) / 16;
-    const int items = min(p.meta[1], p.max_slots) * tiles;
-
-    for (int base = blockIdx.x * IPW; base < items; base += gridDim.x * IPW) {
-        const int item = base + sub;
-        const bool active = item < items;
-        f32x4 acc0[NT], acc1[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            acc0[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc1[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        int s = 0, r0 = 0;
-        if (active) {
-            s = item / tiles;
-            r0 = (item - s * tiles) * 16;
-            const int e = min(max(p.slot_expert[s], 0), p.has_shared ? E : E - 1);
-            const bool shared = e == E && p.has_shared;
-            const uint8_t *wbase;
-            const float *sbase = nullptr;
-            size_t mstride;  // bytes between the gate and up blocks
-            int srow0 = 0, srow1 = 0, sld = 0;
-            if (GU) {
-                wbase = shared ? static_cast<const uint8_t *>(p.Wsh_gu)
-                               : static_cast<const uint8_t *>(p.W_gu) + (size_t)e * 2 * I * H * ESZ;
-                mstride = (size_t)I * H * ESZ;
-                if (WT == 1) {
-                    sld = H / 128;
-                    sbase = shared ? p.ssh_gu : p.s_gu + (size_t)e * (2 * I / 128) * sld;
-                    srow0 = (r0 / 128) * sld;
-                    srow1 = ((I + r0) / 128) * sld;
-                }
-            } else {
-                wbase = shared ? static_cast<const uint8_t *>(p.Wsh_d)
-                               : static_cast<const uint8_t *>(p.W_d) + (size_t)e * H * I * ESZ;
-                mstride = 0;
-                if (WT == 1) {
-                    sld = I / 128;
-                    sbase = shared ? p.ssh_d : p.s_d + (size_t)e * (H / 128) * sld;
-                    srow0 = (r0 / 128) * sld;
-                }
-            }
-            const uint8_t *row0 = wbase + (size_t)(r0 + lr) * K * ESZ + g * 16;
-            const uint8_t *row1 = row0 + mstride;
-            const uint16_t *bbase = GU ? p.xB : p.hB + (size_t)s * I * cols;
-            const uint16_t *bp[NT];
-            bool bvalid[NT];
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const int c = n * 16 + lr;
-                bvalid[n] = c < cols;
-                bp[n] = bbase + (size_t)(g * cols + c) * 8;
-            }
-            const size_t bstep = (size_t)4 * cols * 8;  // elements per k-step
-            const bf16x8 zero8 = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-
-            if (WT == 0) {
-                const int KS = K / 32;
-                const int kb = (kpart * KS) / NKS, ke = ((kpart + 1) * KS) / NKS;
-                for (int ks = kb; ks < ke; ks += KU) {
-                    u32x4 a0[KU], a1[KU];
-                    bf16x8 b[KU][NT];
-#pragma unroll
-                    for (int u = 0; u < KU; ++u) {
-                        if (ks + u < ke) {
-                            a0[u] = ld_nt(row0 + (size_t)(ks + u) * 64);
-                            if (GU) a1[u] = ld_nt(row1 + (size_t)(ks + u) * 64);
-#pragma unroll
-                            for (int n = 0; n < NT; ++n)
-                                b[u][n] = bvalid[n] ? as_bf16x8(*reinterpret_cast<const u32x4 *>(bp[n] + (ks + u) * bstep))
-                                                    : zero8;
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < KU; ++u) {
-                        if (ks + u < ke) {
-#pragma unroll
-                            for (int n = 0; n < NT; ++n) {
-                                acc0[n] = mfma(as_bf16x8(a0[u]), b[u][n], acc0[n]);
-                                if (GU) acc1[n] = mfma(as_bf16x8(a1[u]), b[u][n], acc1[n]);
-                            }
-                        }
-                    }
-                }
-            } else {
-                const int NB = K / 128;
-                const int bb = (kpart * NB) / NKS, be = ((kpart + 1) * NB) / NKS;
-                for (int kb = bb; kb < be; kb += KUB) {
-                    u32x4 a0[KUB][2], a1[KUB][2];
-                    bf16x8 b[KUB][4][NT];
-                    float sc0[KUB], sc1[KUB];
-#pragma unroll
-                    for (int u = 0; u < KUB; ++u) {
-                        if (kb + u < be) {
-#pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                a0[u][h] = ld_nt(row0 + (size_t)(kb + u) * 128 + h * 64);
-                                if (GU) a1[u][h] = ld_nt(row1 + (size_t)(kb + u) * 128 + h * 64);
-                            }
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                                for (int n = 0; n < NT; ++n)
-                                    b[u][q][n] = bvalid[n]
-                                                     ? as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                                                           bp[n] + ((kb + u) * 4 + q) * bstep))
-                                                     : zero8;
-                            sc0[u] = sbase[srow0 + kb + u];
-                            if (GU) sc1[u] = sbase[srow1 + kb + u];
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < KUB; ++u) {
-                        if (kb + u < be) {
-                            f32x4 t0[NT], t1[NT];
-#pragma unroll
-                            for (int n = 0; n < NT; ++n) {
-                                t0[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-                                t1[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-                            }
-#pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                bf16x8 lo, hi;
-                                fp8x16_to_bf16(a0[u][h], lo, hi);
-#pragma unroll
-                                for (int n = 0; n < NT; ++n) {
-                                    t0[n] = mfma(lo, b[u][2 * h][n], t0[n]);
-                                    t0[n] = mfma(hi, b[u][2 * h + 1][n], t0[n]);
-                                }
-                                if (GU) {
-                                    fp8x16_to_bf16(a1[u][h], lo, hi);
-#pragma unroll
-                                    for (int n = 0; n < NT; ++n) {
-                                        t1[n] = mfma(lo, b[u][2 * h][n], t1[n]);
-                                        t1[n] = mfma(hi, b[u][2 * h + 1][n], t1[n]);
-                                    }
-                                }
-                            }
-#pragma unroll
-                            for (int n = 0; n < NT; ++n) {
-                                acc0[n] += sc0[u] * t0[n];
-                                if (GU) acc1[n] += sc1[u] * t1[n];
-                            }
-                        }
-                    }
-                }
+    const int g = lane >> 4, lr = lane & 15;
+    const int T = p.T, H = p.H, I = p.I, E = p.E, cstride = p.cstride, cols = p.cols;
+    const int nkt = H / C::KT;
+    const int rtiles = I / 8;
+    // dynamic LDS, in order: the activation operand (BLDS), the routing
+    // scratch and the token weights (FUSED).  With gu_async_x the operand
+    // has a region of its own and its loads fly while the routing runs;
+    // otherwise the routing scratch overlays the operand region, filled after.
+    const int ksteps = H / 32;
+    const int nx = BLDS ? ksteps * 4 * cols : 0;  // 16-byte operand chunks
+    const size_t xb_bytes = (size_t)nx * 16;
+    const size_t scr_bytes = FUSED ? (RouteScratch::bytes(T, p.k, E, kGuWaves) + 15) & ~(size_t)15 : 0;
+    const bool async_x = BLDS && p.gu_async_x != 0;
+    u32x4 *xs = reinterpret_cast<u32x4 *>(dyn_lds);
+    unsigned char *scr = dyn_lds + (async_x ? xb_bytes : 0);
+    float *tw_lds = reinterpret_cast<float *>(
+        dyn_lds + (async_x ? xb_bytes + scr_bytes : (xb_bytes > scr_bytes ? xb_bytes : scr_bytes)));
+    // direct global -> LDS loads: lane l of a wave fills chunk i0 + l
+    auto stage_x = [&]() {
+        for (int i0 = w * 64; i0 < nx; i0 += kGuWaves * 64) {
+            const int i = i0 + lane;
+            if (i < nx) {
+                const int c = i % cols, kg = i / cols;  // kg = ks * 4 + g
+                load_lds16(p.xB + ((size_t)kg * cstride + c) * 8, xs + i0);
             }
         }
+    };
 
-        if (NKS > 1) {
-            if (active && kpart != 0) {
+    int nslots;
+    if (FUSED) {
+        if (async_x) stage_x();
+        // routing, recomputed by every workgroup (bit-identical results)
+        block_route<kGuWaves * 64>(p, scr, sexp, tw_lds, &nslots_sh, blockIdx.x == 0);
+        nslots = nslots_sh;
+        if (!async_x) stage_x();
+    } else {
+        nslots = min(p.meta[1], p.max_slots);
+        for (int i = threadIdx.x; i < nslots; i += kGuWaves * 64)
+            sexp[i] = min(max(p.slot_expert[i], 0), p.has_shared ? E : E - 1);
+        stage_x();
+    }
+    wait_vm_all();
+    __syncthreads();
+    const int items = nslots * rtiles;
+    if ((int)blockIdx.x >= items) return;
+
+    // Batches of KU consecutive units; batch b of an item belongs to wave
+    // b % kGuWaves, so the workgroup reads one contiguous window that moves
+    // through the item.  Every wave runs the same number of batches per item
+    // (trailing ones empty), so the reduction barriers line up.
+    const int nunits = WT == 1 ? nkt / 2 : nkt;
+    const int nbi = (nunits + KU - 1) / KU;                 // batches per item
+    const int nb = (nbi + kGuWaves - 1) / kGuWaves;         // per wave per item
+    const int my_items = (items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int F = my_items * nb;
+    const size_t esz = WT == 1 ? 1 : 2;
+    const size_t bstep = (size_t)4 * cstride * 8;                       // global: elements per k-step
+    const uint16_t *xb = p.xB + (size_t)g * cstride * 8;                // global: lane group, k-step 0
+    int coff[NT];
+    col_offsets<NT>(coff, lr, cols);
+
+    auto load_batch = [&](B &bt, int f) {
+        const int item = blockIdx.x + (f / nb) * gridDim.x;
+        const int s = item / rtiles, rt = item - s * rtiles;
+        const int e = sexp[s];
+        const bool sh = e == E;
+        const uint8_t *tiles = (sh ? static_cast<const uint8_t *>(p.Wsh_gu)
+                                   : static_cast<const uint8_t *>(p.W_gu) + (size_t)e * 2 * I * H * esz) +
+                               (size_t)rt * nkt * 1024 + lane * 16;
+        const float *srow = nullptr;
+        if (WT == 1) {
+            const int sld = H / 128;
+            const float *sb = sh ? p.ssh_gu : p.s_gu + (size_t)e * (2 * I / 128) * sld;
+            srow = sb + (size_t)((g < 2 ? 8 * rt : I + 8 * rt) / 128) * sld;
+        }
+        const int k0 = ((f % nb) * kGuWaves + w) * KU;
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int kk = k0 + u;
+            const bool on = kk < nunits;
+            const int kc = on ? kk : nunits - 1;
+            bt.on[u] = on;
+#pragma unroll
+            for (int h = 0; h < B::NA; ++h) bt.a[u][h] = ld_nt(tiles + (size_t)kc * C::USTEP + h * 1024);
+#pragma unroll
+            for (int q = 0; q < B::NS; ++q) {
+                const int ks = kc * B::NS + q;
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    red[w][n][lane] = acc0[n];
-                    if (GU) red[w][NT + n][lane] = acc1[n];
+                    if (BLDS)
+                        bt.b[u][q][n] = xs[(ks * 4 + g) * cols + (coff[n] >> 3)];
+                    else
+                        bt.b[u][q][n] = *reinterpret_cast<const u32x4 *>(xb + (size_t)ks * bstep + coff[n]);
                 }
             }
-            __syncthreads();
-            if (active && kpart == 0) {
+            bt.sc[u] = WT == 1 ? srow[kc] : 0.f;
+        }
+    };
+    // End of an item: every wave stores its partial sums into one of two
+    // LDS buffers (alternating per item) and passes ONE barrier; then 8 x T
+    // threads, starting at a wave that rotates with the item, each finish one
+    // (intermediate row, token) output from the buffer while the other waves
+    // keep streaming.  The
+    // buffer of item i is rewritten at item i + 2 only, after every wave has
+    // passed the barrier of item i + 1, i.e. after the readers of item i.
+    auto finish_item = [&](f32x4 (&acc2)[2][NT], int f) {
+        const int ii = f / nb;
+        const int item = blockIdx.x + ii * gridDim.x;
+        const int s = item / rtiles, rt = item - s * rtiles;
+        const int buf = ii & 1;
+        fold_acc<NT>(acc2);
 #pragma unroll
-                for (int q = 1; q < NKS; ++q) {
+        for (int n = 0; n < NT; ++n) red[buf][w][n][lane] = acc2[0][n];
+        __syncthreads();
+        const int nthr = kGuWaves * 64;
+        const int o = ((int)threadIdx.x - (ii % kGuWaves) * 64 + nthr) % nthr;  // rotating owner wave
+        if (o < 8 * T) {
+            // output (intermediate row il = 8 rt + r, token t); D row r is gate,
+            // D row 8 + r is up; column t (hi) and T + t (lo, split mode)
+            const int r = o / T, t = o - r * T;
+            float gv = 0.f, uv = 0.f;
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) {
-                        acc0[n] += red[w + q][n][lane];
-                        if (GU) acc1[n] += red[w + q][NT + n][lane];
-                    }
+            for (int part = 0; part < (SPLIT ? 2 : 1); ++part) {
+                const int c = part ? T + t : t;
+                const int n = c >> 4, col = c & 15;
+                const int lg = 16 * (r >> 2) + col, lu = 16 * (2 + (r >> 2)) + col, j = r & 3;
+#pragma unroll
+                for (int q = 0; q < kGuWaves; ++q) {
+                    gv += red[buf][q][n][lg][j];
+                    uv += red[buf][q][n][lu][j];
                 }
+            }
+            const float wt = FUSED ? tw_lds[s * T + t] : p.tokw[(size_t)s * T + t];
+            const float hv = wt * (silu(gv) * uv);
+            const uint16_t hi = f32_to_bf16_rne(hv);
+            uint16_t *hb = p.hB + (size_t)s * I * cstride;
+            const int il = 8 * rt + r;
+            hb[b_index(il, t, cstride, WT == 1)] = hi;
+            if (SPLIT) hb[b_index(il, T + t, cstride, WT == 1)] = f32_to_bf16_rne(hv - bf16_to_f32(hi));
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc2[0][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    f32x4 acc[2][NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[0][n] = acc[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Two register buffers; the prefetch is issued unconditionally (clamped
+    // to the last batch) so the number of loads in flight is static.
+    B b0, b1;
+    load_batch(b0, 0);
+    for (int f = 0; f < F; f += 2) {
+        load_batch(b1, min(f + 1, F - 1));
+        compute_batch<WT, NT, KU>(b0, acc, true);
+        if (f % nb == nb - 1) finish_item(acc, f);
+        load_batch(b0, min(f + 2, F - 1));
+        const bool v1 = f + 1 < F;
+        compute_batch<WT, NT, KU>(b1, acc, v1);
+        if (v1 && (f + 1) % nb == nb - 1) finish_item(acc, f + 1);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// down: one workgroup of 8 waves per output row tile (16 rows of H).  The
+// workgroup streams the row tile of EVERY union slot (the waves take
+// interleaved batches of it), accumulating y for all tokens in registers
+// (the gate weights are already folded into the hidden activations); the
+// partial sums meet in LDS in a fixed order and the tile of y is written
+// once.  No atomics, no second pass, equal bytes per workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kDnWaves = 8;
+
+template <int WT, int NT, bool SPLIT>
+__global__ __launch_bounds__(kDnWaves * 64) void down_kernel(VerifyParams p) {
+    using C = UnitCfg<WT, NT>;
+    constexpr int KU = C::KU;
+    using B = Batch<WT, NT, KU>;
+    __shared__ f32x4 red[kDnWaves][NT][64];
+    __shared__ int sexp[kMaxExperts + 1];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = lane >> 4, lr = lane & 15;
+    const int T = p.T, H = p.H, I = p.I, E = p.E, cstride = p.cstride;
+    const int nkt = I / C::KT;
+    const int rtiles = H / 16;
+    const int nslots = min(p.meta[1], p.max_slots);
+    const size_t esz = WT == 1 ? 1 : 2;
+    const size_t bstep = (size_t)4 * cstride * 8;
+    for (int i = threadIdx.x; i < nslots; i += kDnWaves * 64)
+        sexp[i] = min(max(p.slot_expert[i], 0), p.has_shared ? E : E - 1);
+    __syncthreads();
+    // Units (slot, k-unit) in slot-major order for one row tile; batches of KU
+    // consecutive units go to the waves round-robin, so the workgroup reads
+    // one contiguous window that moves through the slots' row-tile segments.
+    const int nunits = WT == 1 ? nkt / 2 : nkt;
+    const int total = nslots * nunits;
+    const int nbt = (total + KU - 1) / KU;
+    const int nbw = nbt > w ? (nbt - w + kDnWaves - 1) / kDnWaves : 0;  // this wave's batches
+    const int sld = I / 128;
+    const uint16_t *hb0 = p.hB + (size_t)g * cstride * 8;
+    int coff[NT];
+    col_offsets<NT>(coff, lr, p.cols);
+    for (int rt = blockIdx.x; rt < rtiles; rt += gridDim.x) {
+        const size_t toff = (size_t)rt * nkt * 1024 + lane * 16;
+        const int srow = (16 * rt) / 128;
+        auto load_batch = [&](B &bt, int f) {
+            const int q0 = (f * kDnWaves + w) * KU;
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                const int q = q0 + u;
+                const bool on = q < total;
+                const int qc = on ? q : total - 1;
+                const int s = qc / nunits, kk = qc - s * nunits;
+                const int e = sexp[s];
+                const bool sh = e == E;
+                const uint8_t *wb = sh ? static_cast<const uint8_t *>(p.Wsh_d)
+                                       : static_cast<const uint8_t *>(p.W_d) + (size_t)e * H * I * esz;
+                const float scale = WT == 1 ? (sh ? p.ssh_d : p.s_d + (size_t)e * (H / 128) * sld)[srow * sld + kk] : 0.f;
+                load_unit<WT, NT, KU>(bt, u, on, wb + toff + (size_t)kk * C::USTEP,
+                                      hb0 + (size_t)s * I * cstride + (size_t)kk * C::KSTEPS * bstep, bstep, scale, coff);
+            }
+        };
+        f32x4 acc2[2][NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc2[0][n] = acc2[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 (&acc)[NT] = acc2[0];
+        if (nbw > 0) {
+            B b0, b1;
+            load_batch(b0, 0);
+            for (int f = 0; f < nbw; f += 2) {
+                load_batch(b1, min(f + 1, nbw - 1));
+                compute_batch<WT, NT, KU>(b0, acc2, true);
+                load_batch(b0, min(f + 2, nbw - 1));
+                compute_batch<WT, NT, KU>(b1, acc2, f + 1 < nbw);
             }
         }
-
-        if (active && kpart == 0) {
-            const bool fp8 = WT == 1;
-            // Column c of tile n is token n * 16 + lr.  In split mode the low
-            // part of token t sits in column T + t (tile (T + t) / 16, lane
-            // (T + t) % 16 of the same lane group) and is added here.
-            float v0[NT][4], v1[NT][4];
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v0[n][j] = acc0[n][j];
-                    v1[n][j] = acc1[n][j];
-                }
-            if (SPLIT) {
-#pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    const int clo = T + n * 16 + lr;
-                    const int nlo = clo >> 4;
-                    const int src = (lane & ~15) | (clo & 15);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float lo0 = 0.f, lo1 = 0.f;
-#pragma unroll
-                        for (int q = 0; q < NT; ++q) {
-                            const float a = __shfl(acc0[q][j], src);
-                            const float b = GU ? __shfl(acc1[q][j], src) : 0.f;
-                            if (q == nlo) {
-                                lo0 = a;
-                                lo1 = b;
-                            }
-                        }
-                        v0[n][j] += lo0;
-                        v1[n][j] += lo1;
-                    }
-                }
-            }
+        fold_acc<NT>(acc2);
+        reduce_waves<NT, kDnWaves>(acc, red, w, lane);
+        if (w == 0) {
+            float v[NT][4];
+            combine_split<NT, SPLIT>(v, acc, T, lane);
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
                 const int t = n * 16 + lr;
-                if (t < T) {
-                    if (GU) {
-                        const float wt = p.tokw[(size_t)s * T + t];
-                        float hv[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) hv[j] = wt * (silu(v0[n][j]) * v1[n][j]);
-                        uint16_t hi[4], lo[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            hi[j] = f32_to_bf16_rne(hv[j]);
-                            lo[j] = f32_to_bf16_rne(hv[j] - bf16_to_f32(hi[j]));
-                        }
-                        uint16_t *hb = p.hB + (size_t)s * I * cols;
-                        const int i = r0 + 4 * g;
-                        *reinterpret_cast<u32x2 *>(hb + b_index(i, t, cols, fp8)) =
-                            u32x2{(unsigned)hi[0] | ((unsigned)hi[1] << 16), (unsigned)hi[2] | ((unsigned)hi[3] << 16)};
-                        if (SPLIT)
-                            *reinterpret_cast<u32x2 *>(hb + b_index(i, T + t, cols, fp8)) =
-                                u32x2{(unsigned)lo[0] | ((unsigned)lo[1] << 16), (unsigned)lo[2] | ((unsigned)lo[3] << 16)};
-                    } else {
-                        const int pos = p.tokpos[(size_t)s * T + t];
-                        if (pos >= 0 && pos < T * p.k + T)
-                            *reinterpret_cast<float4 *>(p.ydown + (size_t)pos * H + r0 + 4 * g) =
-                                make_float4(v0[n][0], v0[n][1], v0[n][2], v0[n][3]);
-                    }
-                }
+                if (t < T)
+                    *reinterpret_cast<float4 *>(p.y + (size_t)t * H + 16 * rt + 4 * g) =
+                        make_float4(v[n][0], v[n][1], v[n][2], v[n][3]);
             }
         }
-        if (NKS > 1) __syncthreads();
+        __syncthreads();
     }
 }
 
@@ -414,21 +586,60 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyParams p) {
     }
 }
 
-// Persistent grid: as many workgroups as fit on the device at once.
+// Persistent grid: `per_cu` workgroups per compute unit, at most what fits.
 template <typename K>
-int resident_grid(K kernel, int n_cu) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kFfnThreads, 0) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    return per_cu * n_cu;
+int resident_grid(K kernel, int threads, int n_cu, int per_cu, size_t dyn_lds) {
+    int fit = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, kernel, threads, dyn_lds) != hipSuccess || fit < 1) fit = 1;
+    return (per_cu < fit ? per_cu : fit) * n_cu;
+}
+
+// LDS plan of the gate-up kernel: routing fused into its prologue and the
+// activation operand held in LDS when they fit in one compute unit.
+struct GuPlan {
+    bool fused, blds, async_x;
+    size_t dyn;
+};
+
+GuPlan plan_gateup(const VerifyParams &p) {
+    const int nt = (p.cols + 15) / 16;
+    const size_t stat = sizeof(float) * 4 * 2 * kGuWaves * nt * 64 + sizeof(int) * (kMaxExperts + 2);
+    auto al = [](size_t v) { return (v + 15) & ~(size_t)15; };
+    const size_t scr = al(RouteScratch::bytes(p.T, p.k, p.E, kGuWaves));
+    const size_t tw = (size_t)p.max_slots * p.T * sizeof(float);
+    const size_t xb = (size_t)(p.H / 32) * 4 * p.cols * 16;
+    const size_t over = xb > scr ? xb : scr;
+    if (xb + scr + tw + stat <= kLdsPerCu) return {true, true, true, xb + scr + tw};
+    if (over + tw + stat <= kLdsPerCu) return {true, true, false, over + tw};
+    if (scr + tw + stat <= kLdsPerCu) return {true, false, false, scr + tw};
+    return {false, false, false, 0};
+}
+
+template <typename K>
+hipError_t launch_gu(K kernel, const VerifyParams &p, size_t dyn, int n_cu, hipStream_t s) {
+    if (dyn > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)dyn) != hipSuccess)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kernel, dim3(n_cu * kGateUpWgPerCu), dim3(kGuWaves * 64), dyn, s, p);
+    return hipGetLastError();
 }
 
 template <int WT, int NT, bool SPLIT, bool GU>
 hipError_t launch_one(const VerifyParams &p, int n_cu, hipStream_t s) {
-    constexpr int NKS = GU ? 4 : 1;
-    auto kernel = ffn_mfma_kernel<WT, NT, SPLIT, NKS, GU>;
-    static const int grid = resident_grid(kernel, n_cu);
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kFfnThreads), 0, s, p);
+    if (GU) {
+        const GuPlan pl = plan_gateup(p);
+        VerifyParams q = p;
+        q.gu_async_x = pl.async_x ? 1 : 0;
+        if (pl.fused && pl.blds) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true>, q, pl.dyn, n_cu, s);
+        if (pl.fused) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, false>, q, pl.dyn, n_cu, s);
+        return launch_gu(gateup_kernel<WT, NT, SPLIT, false, false>, q, 0, n_cu, s);
+    } else {
+        auto kernel = down_kernel<WT, NT, SPLIT>;
+        static const int cap = resident_grid(kernel, kDnWaves * 64, n_cu, kDownWgPerCu, 0);
+        const int rtiles = p.H / 16;  // one workgroup per row tile when they all fit at once
+        hipLaunchKernelGGL(kernel, dim3(rtiles < cap ? rtiles : cap), dim3(kDnWaves * 64), 0, s, p);
+    }
     return hipGetLastError();
 }
 
@@ -453,6 +664,8 @@ hipError_t launch_mfma(const VerifyParams &p, int n_cu, hipStream_t s) {
 
 }  // namespace
 
+bool gateup_fuses_routing(const VerifyParams &p) { return p.wdtype != 0 && plan_gateup(p).fused; }
+
 hipError_t launch_gateup(const VerifyParams &p, int n_cu, hipStream_t s) {
     const int grid = n_cu * 4;
     if (p.wdtype == 0) {
@@ -472,6 +685,7 @@ hipError_t launch_down(const VerifyParams &p, int n_cu, hipStream_t s) {
 }
 
 hipError_t launch_combine(const VerifyParams &p, hipStream_t s) {
+    if (p.wdtype != 0) return hipSuccess;  // the matrix-core down kernel writes y itself
     int blocks = (p.T * p.H + 255) / 256;
     if (blocks > 1024) blocks = 1024;
     hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, p);

@@ -9,11 +9,13 @@ namespace moe {
 // Everything one verify-layer call needs, passed by value to every kernel.
 struct VerifyParams {
     int T, H, I, E, k, wdtype;
-    int cols;        // compact B-operand columns: 2T (high/low split) or T
+    int cols;        // B-operand columns in use: 2T (high/low split) or T
+    int cstride;     // B-operand column stride (= cols; lanes past the used columns clamp)
     int split;       // 1 if activations enter the products as a bf16 hi/lo pair
     int has_shared;  // always-on shared expert present
     int bias_on, cap;
     int max_slots;   // min(E, T k) + has_shared: bound on the device slot count
+    int gu_async_x;  // gate-up: operand staging runs alongside the routing (own LDS region)
     float alpha;
 
     const float *x, *Wr;
@@ -49,8 +51,11 @@ constexpr int kWaveSize = 64;
 hipError_t launch_router(const VerifyParams &p, hipStream_t s);
 hipError_t launch_route(const VerifyParams &p, hipStream_t s);
 hipError_t launch_gateup(const VerifyParams &p, int n_cu, hipStream_t s);
+bool gateup_fuses_routing(const VerifyParams &p);  // routing runs in the gate-up prologue
 hipError_t launch_down(const VerifyParams &p, int n_cu, hipStream_t s);
 hipError_t launch_combine(const VerifyParams &p, hipStream_t s);
+hipError_t launch_pack(const void *src, void *dst, int E, int R, int K, int esz, int interleave, int half,
+                       hipStream_t s);
 hipError_t launch_union_stats(const int32_t *topk_idx, int nL, int T, int k, int E, int32_t *counts,
                               float *reuse, hipStream_t s);
 hipError_t launch_select(int N, const float *P, const uint32_t *F, int W, int gamma, float eps,

@@ -56,6 +56,7 @@ Layout make_layout(const moe_layer &L, int T) {
     const size_t E = L.E, k = L.k, H = L.H, I = L.I;
     const size_t slots = (size_t)std::min<long>(L.E, (long)T * L.k) + 1;
     const size_t cols = split_mode(T) ? 2 * T : T;
+    const size_t cstride = cols;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -79,8 +80,8 @@ Layout make_layout(const moe_layer &L, int T) {
         o.xB = o.hB = 0;
         o.h32 = take(slots * T * I * 4);
     } else {
-        o.xB = take(H * cols * 2);
-        o.hB = take(slots * I * cols * 2);
+        o.xB = take(H * cstride * 2);
+        o.hB = take(slots * I * cstride * 2);
         o.h32 = 0;
     }
     o.ydown = take(((size_t)T * k + T) * H * 4);
@@ -157,6 +158,7 @@ int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const mo
     p.wdtype = L.wdtype;
     p.split = split_mode(T) ? 1 : 0;
     p.cols = p.split ? 2 * T : T;
+    p.cstride = p.cols;
     p.has_shared = L.Wsh_gu != nullptr;
     p.max_slots = std::min(L.E, T * L.k) + p.has_shared;
     p.bias_on = bias != nullptr;
@@ -211,7 +213,7 @@ int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const mo
     if (!mark(0)) return fail(MOE_EHIP, "hipEventRecord failed");
     if ((err = moe::launch_router(p, s)) != hipSuccess) goto hip_fail;
     if (!mark(1)) return fail(MOE_EHIP, "hipEventRecord failed");
-    if ((err = moe::launch_route(p, s)) != hipSuccess) goto hip_fail;
+    if (!moe::gateup_fuses_routing(p) && (err = moe::launch_route(p, s)) != hipSuccess) goto hip_fail;
     if (!mark(2)) return fail(MOE_EHIP, "hipEventRecord failed");
     if ((err = moe::launch_gateup(p, ncu, s)) != hipSuccess) goto hip_fail;
     if (!mark(3)) return fail(MOE_EHIP, "hipEventRecord failed");
@@ -222,6 +224,26 @@ int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const mo
     return MOE_OK;
 hip_fail:
     return fail(MOE_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+}
+
+int moe_pack_weights(const void *src, void *dst, int32_t E, int32_t rows, int32_t K, int32_t wdtype,
+                     int32_t gate_up, void *stream) {
+    if (!src || !dst) return fail(MOE_EINVAL, "NULL pointer");
+    if (wdtype != MOE_BF16 && wdtype != MOE_FP8_E4M3) return fail(MOE_EINVAL, "packing covers bf16 and fp8 weights");
+    if (E < 1 || rows < 16 || K < 1) return fail(MOE_EINVAL, "need E >= 1, rows >= 16, K >= 1");
+    const int kt = wdtype == MOE_BF16 ? 32 : 64;
+    if (rows % 16 != 0 || K % kt != 0)
+        return fail(MOE_EINVAL, "rows must be a multiple of 16 and K of %d", kt);
+    if (gate_up && rows % 32 != 0) return fail(MOE_EINVAL, "gate-up rows (2I) must be a multiple of 32");
+    const size_t esz = wdtype == MOE_BF16 ? 2 : 1;
+    const size_t bytes = (size_t)E * rows * K * esz;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + bytes && b < a + bytes) return fail(MOE_EINVAL, "src and dst overlap");
+    if ((a | b) & 15) return fail(MOE_EINVAL, "src and dst must be 16-byte aligned");
+    hipError_t err = moe::launch_pack(src, dst, E, rows, K, (int)esz, gate_up ? 1 : 0, rows / 2,
+                                      static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(MOE_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return MOE_OK;
 }
 
 int union_stats(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32_t E, int32_t *counts,
@@ -247,7 +269,7 @@ int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32
     for (int i = 0; i < N; ++i)
         if (parent[i] < -1 || parent[i] >= i)
             return fail(MOE_EINVAL, "parent[%d]=%d: nodes must be in BFS order (parent < child)", i, parent[i]);
-    if ((size_t)N * W + W + (N + 31) / 32 > (size_t)moe::kSelectMaxLdsWords)
+    if ((size_t)N * W + W + N + (N + 31) / 32 > (size_t)moe::kSelectMaxLdsWords)
         return fail(MOE_ENOTSUP, "tree footprint of %d x %d words exceeds the %d-word LDS stage", N, W,
                     moe::kSelectMaxLdsWords);
     if (nt == 0 || gamma == 0) return MOE_OK;  // nothing to write

@@ -1,0 +1,57 @@
+// Packing of expert weights into the matrix-core tile layout that the FFN
+// kernels stream.  One-time weight preparation, not part of a verify call.
+//
+// A tile is 1 KB: 16 rows x 32 k (bf16) or 16 rows x 64 k (fp8).  Inside a
+// tile, 16-byte lane slot l (l = 0..63) holds row m = l % 16 and the k-range
+// [8 g, 8 g + 8) (bf16) or [16 g, 16 g + 16) (fp8) of the tile, g = l / 16:
+// exactly the A operand of v_mfma_f32_16x16x32_bf16 for lane l, so one
+// 16-byte load per lane reads 1 KB of contiguous memory per wave.  Tiles are
+// ordered row-tile major, K-tile minor, so one row tile is one contiguous
+// stream.  For gate/up matrices a row tile interleaves 8 gate rows (tile rows
+// 0..7) with the 8 up rows of the same intermediate indices (tile rows 8..15),
+// so one tile yields both halves of SwiGLU for 8 intermediate indices.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
+                                                   long long n_slots, int R, int K, int esz, int interleave,
+                                                   int half) {
+    // one thread per 16-byte lane slot of the packed output
+    const int KT = esz == 2 ? 32 : 64;
+    const int nkt = K / KT;
+    const long long per_expert = (long long)(R / 16) * nkt * 64;
+    for (long long q = (long long)blockIdx.x * 256 + threadIdx.x; q < n_slots; q += (long long)gridDim.x * 256) {
+        const long long e = q / per_expert;
+        const long long rem = q - e * per_expert;
+        const int l = (int)(rem & 63);
+        const long long tile = rem >> 6;
+        const int rt = (int)(tile / nkt), kt = (int)(tile - (long long)rt * nkt);
+        const int m = l & 15, g = l >> 4;
+        int row;
+        if (interleave)
+            row = m < 8 ? 8 * rt + m : half + 8 * rt + (m - 8);
+        else
+            row = 16 * rt + m;
+        const int k = kt * KT + g * (KT / 4);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(src + ((e * R + row) * (long long)K + k) * esz);
+        *reinterpret_cast<u32x4 *>(dst + q * 16) = v;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pack(const void *src, void *dst, int E, int R, int K, int esz, int interleave, int half,
+                       hipStream_t s) {
+    const long long n_slots = (long long)E * (R / 16) * (K / (esz == 2 ? 32 : 64)) * 64;
+    long long blocks = (n_slots + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) return hipSuccess;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const uint8_t *>(src),
+                       static_cast<uint8_t *>(dst), n_slots, R, K, esz, interleave, half);
+    return hipGetLastError();
+}
+
+}  // namespace moe

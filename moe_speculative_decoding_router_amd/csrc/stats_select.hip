@@ -39,62 +39,86 @@ __global__ __launch_bounds__(256) void union_stats_kernel(const int32_t *__restr
     }
 }
 
-// One wave per tree.  The tree's footprints are staged in LDS with 16-byte
-// loads; the buffer B and the chosen set live in LDS too.  For each node the
-// 64 lanes popcount consecutive words of F & ~B and the count is reduced
-// across the wave, so every score is computed identically in all lanes.
-__global__ __launch_bounds__(64) void select_kernel(int N, const float *__restrict__ P,
-                                                    const uint32_t *__restrict__ F, int W, int gamma,
-                                                    float eps, int nt, int32_t *S) {
+// One workgroup (256 threads) per tree.  The tree's footprints are staged in
+// LDS with 16-byte loads.  Each round, groups of TPN threads (a power of two
+// dividing the wave) popcount the words of F & ~B of their nodes and reduce
+// the count inside the group, so every node is scored in parallel; wave 0
+// then takes the arg-max in (score desc, node asc) order and all threads add
+// the chosen footprint to B.
+constexpr int kSelThreads = 256;
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(int N, const float *__restrict__ P,
+                                                             const uint32_t *__restrict__ F, int W, int gamma,
+                                                             float eps, int nt, int tpn, int32_t *S) {
     extern __shared__ uint32_t lds[];
-    uint32_t *Fs = lds;                    // [N * W]
-    uint32_t *Bs = Fs + (size_t)N * W;     // [W]
-    uint32_t *chosen = Bs + W;             // [ceil(N / 32)]
-    const int lane = threadIdx.x;
+    uint32_t *Fs = lds;                                   // [N * W]
+    uint32_t *Bs = Fs + (size_t)N * W;                    // [W]
+    float *sc = reinterpret_cast<float *>(Bs + W);        // [N]
+    uint32_t *chosen = reinterpret_cast<uint32_t *>(sc + N);  // [ceil(N / 32)]
+    __shared__ int best_sh;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int tree = blockIdx.x;
     if (tree >= nt) return;
     const uint32_t *Ft = F + (size_t)tree * N * W;
     const float *Pt = P + (size_t)tree * N;
     const int nwords = N * W;
-    const bool aligned16 = ((nwords & 3) == 0) && ((reinterpret_cast<uintptr_t>(Ft) & 15) == 0);
-    if (aligned16) {
+    if (((nwords & 3) == 0) && ((reinterpret_cast<uintptr_t>(Ft) & 15) == 0)) {
+        // every load of a thread is issued before its LDS stores (one round trip)
+        constexpr int kPer = kSelectMaxLdsWords / 4 / kSelThreads;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(Ft);
         u32x4 *dst = reinterpret_cast<u32x4 *>(Fs);
-        for (int i = lane; i < nwords / 4; i += 64) dst[i] = __builtin_nontemporal_load(src + i);
+        const int n4 = nwords / 4;
+        u32x4 v[kPer];
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) v[r] = __builtin_nontemporal_load(src + min(tid + r * kSelThreads, n4 - 1));
+#pragma unroll
+        for (int r = 0; r < kPer; ++r)
+            if (tid + r * kSelThreads < n4) dst[tid + r * kSelThreads] = v[r];
     } else {
-        for (int i = lane; i < nwords; i += 64) Fs[i] = Ft[i];
+        for (int i = tid; i < nwords; i += kSelThreads) Fs[i] = Ft[i];
     }
-    for (int i = lane; i < W; i += 64) Bs[i] = 0u;
-    for (int i = lane; i < (N + 31) / 32; i += 64) chosen[i] = 0u;
+    for (int i = tid; i < W; i += kSelThreads) Bs[i] = 0u;
+    for (int i = tid; i < (N + 31) / 32; i += kSelThreads) chosen[i] = 0u;
     __syncthreads();
 
+    const int grp = tid / tpn, sub = tid - grp * tpn, ngrp = kSelThreads / tpn;
     for (int r = 0; r < gamma; ++r) {
-        int best = -1;
-        float best_s = -INFINITY;
-        for (int n = 0; n < N; ++n) {
-            if ((chosen[n >> 5] >> (n & 31)) & 1u) continue;
+        // ---- score every node (groups of tpn threads per node) ----
+        for (int n0 = 0; n0 < N; n0 += ngrp) {
+            const int n = n0 + grp;
             int c = 0;
-            for (int i = lane; i < W; i += 64) c += __popc(Fs[(size_t)n * W + i] & ~Bs[i]);
-            c = wave_sum_int(c);
-            const float sc = __fdiv_rn(Pt[n], __fadd_rn((float)c, eps));
-            if (sc > best_s) {  // strict: equal scores keep the lower node index
-                best_s = sc;
-                best = n;
-            }
-        }
-        if (best < 0) {  // only reachable with NaN probabilities: lowest unchosen node
-            for (int n = 0; n < N; ++n)
-                if (!((chosen[n >> 5] >> (n & 31)) & 1u)) {
-                    best = n;
-                    break;
-                }
+            if (n < N)
+                for (int i = sub; i < W; i += tpn) c += __popc(Fs[(size_t)n * W + i] & ~Bs[i]);
+            for (int off = tpn >> 1; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+            if (n < N && sub == 0) sc[n] = __fdiv_rn(Pt[n], __fadd_rn((float)c, eps));
         }
         __syncthreads();
-        if (lane == 0) {
-            S[(size_t)tree * gamma + r] = best;
-            chosen[best >> 5] |= 1u << (best & 31);
+        // ---- arg-max over unchosen nodes: (score desc, node asc) ----
+        if (wv == 0) {
+            float bv = -INFINITY;
+            int bi = INT_MAX;
+            for (int n = lane; n < N; n += 64) {
+                if ((chosen[n >> 5] >> (n & 31)) & 1u) continue;
+                const float v = sc[n] != sc[n] ? -INFINITY : sc[n];
+                if (better(v, n, bv, bi)) {
+                    bv = v;
+                    bi = n;
+                }
+            }
+            wave_argmax(bv, bi);
+            if (lane == 0) {
+                if (bi < 0 || bi >= N) {  // unreachable for N > r; kept memory-safe
+                    bi = 0;
+                    while (bi < N - 1 && ((chosen[bi >> 5] >> (bi & 31)) & 1u)) ++bi;
+                }
+                best_sh = bi;
+                S[(size_t)tree * gamma + r] = bi;
+                chosen[bi >> 5] |= 1u << (bi & 31);
+            }
         }
-        for (int i = lane; i < W; i += 64) Bs[i] |= Fs[(size_t)best * W + i];
+        __syncthreads();
+        const int best = best_sh;
+        for (int i = tid; i < W; i += kSelThreads) Bs[i] |= Fs[(size_t)best * W + i];
         __syncthreads();
     }
 }
@@ -110,8 +134,11 @@ hipError_t launch_union_stats(const int32_t *topk_idx, int nL, int T, int k, int
 
 hipError_t launch_select(int N, const float *P, const uint32_t *F, int W, int gamma, float eps, int nt,
                          int32_t *S, hipStream_t s) {
-    const size_t lds = ((size_t)N * W + W + (N + 31) / 32) * 4;
-    hipLaunchKernelGGL(select_kernel, dim3(nt), dim3(64), lds, s, N, P, F, W, gamma, eps, nt, S);
+    const size_t lds = ((size_t)N * W + W + N + (N + 31) / 32) * 4;
+    // threads per node: the largest power of two <= min(64, 256 / N), at least 1
+    int tpn = 1;
+    while (tpn * 2 <= 64 && tpn * 2 * N <= kSelThreads) tpn *= 2;
+    hipLaunchKernelGGL(select_kernel, dim3(nt), dim3(kSelThreads), lds, s, N, P, F, W, gamma, eps, nt, tpn, S);
     return hipGetLastError();
 }
 

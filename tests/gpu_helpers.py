@@ -57,7 +57,7 @@ def expert_fn_raw(wl: synth.Workload, layer: int):
 
 
 def device_layer(wl: synth.Workload, layer: int, Wr: np.ndarray):
-    W = synth.fill_layer_device(wl, layer, torch_dev())
+    W = m.pack_layer_tensors(synth.fill_layer_device(wl, layer, torch_dev()), wl.wdtype)
     return m.LayerWeights(H=wl.H, I=wl.I, E=wl.E, k=wl.k, wdtype=wl.wdtype, Wr=to_dev(Wr), **W)
 
 

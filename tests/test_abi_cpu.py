@@ -28,7 +28,7 @@ def lib():
     return m.lib()
 
 
-def test_exports_every_declared_symbol(lib):
+def test_exports_every_declared_symbol(lib):  # noqa: D103
     names = declared_functions()
     assert set(names) == set(m.EXPORTED), names
     for n in names:

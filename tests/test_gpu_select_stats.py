@@ -85,3 +85,41 @@ def test_device_fill_matches_host_generator(kind):
     torch.cuda.synchronize()
     host = synth.host_fill(kind, n_exp, per, seed=0, layer=5, expert0=9, matrix=1)
     assert np.array_equal(buf.cpu().numpy().view(host.dtype), host)
+
+
+def expected_pack(src, gate_up, esz):
+    """The tile layout as the header describes it, written with NumPy."""
+    E, R, K = src.shape
+    KT = 32 if esz == 2 else 64
+    out = np.empty(E * R * K * esz, dtype=np.uint8)
+    b = src.view(np.uint8).reshape(E, R, K * esz)
+    q = 0
+    for e in range(E):
+        for rt in range(R // 16):
+            for kt in range(K // KT):
+                for l in range(64):
+                    m_, g = l % 16, l // 16
+                    if gate_up:
+                        row = 8 * rt + m_ if m_ < 8 else R // 2 + 8 * rt + (m_ - 8)
+                    else:
+                        row = 16 * rt + m_
+                    k = kt * KT + g * (KT // 4)
+                    out[q * 16:(q + 1) * 16] = b[e, row, k * esz:k * esz + 16]
+                    q += 1
+    return out
+
+
+@pytest.mark.parametrize("wdtype,gate_up", [("bf16", True), ("bf16", False), ("fp8", True), ("fp8", False)])
+def test_pack_layout(wdtype, gate_up):
+    rng = np.random.default_rng(7)
+    E, R, K = 2, 64, 256
+    if wdtype == "bf16":
+        src = rng.integers(0, 1 << 16, size=(E, R, K), dtype=np.uint16)
+        t = to_dev(src.view(np.int16))
+    else:
+        src = rng.integers(0, 256, size=(E, R, K), dtype=np.uint8)
+        t = to_dev(src)
+    out = m.pack_weights(t, wdtype, gate_up)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint8).ravel()
+    assert np.array_equal(got, expected_pack(src, gate_up, 2 if wdtype == "bf16" else 1))
