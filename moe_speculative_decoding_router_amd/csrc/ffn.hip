@@ -305,20 +305,30 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     int coff[NT];
     col_offsets<NT>(coff, lr, cols);
 
+    // Tile and scale pointers of the item being loaded, refreshed once per
+    // item (batches are loaded in increasing order).
+    int c_ord = -1;
+    const uint8_t *c_tiles = nullptr;
+    const float *c_srow = nullptr;
     auto load_batch = [&](B &bt, int f) {
-        const int item = blockIdx.x + (f / nb) * gridDim.x;
-        const int s = item / rtiles, rt = item - s * rtiles;
-        const int e = sexp[s];
-        const bool sh = e == E;
-        const uint8_t *tiles = (sh ? static_cast<const uint8_t *>(p.Wsh_gu)
-                                   : static_cast<const uint8_t *>(p.W_gu) + (size_t)e * 2 * I * H * esz) +
-                               (size_t)rt * nkt * 1024 + lane * 16;
-        const float *srow = nullptr;
-        if (WT == 1) {
-            const int sld = H / 128;
-            const float *sb = sh ? p.ssh_gu : p.s_gu + (size_t)e * (2 * I / 128) * sld;
-            srow = sb + (size_t)((g < 2 ? 8 * rt : I + 8 * rt) / 128) * sld;
+        const int ord = f / nb;
+        if (ord != c_ord) {
+            c_ord = ord;
+            const int item = blockIdx.x + ord * gridDim.x;
+            const int s = item / rtiles, rt = item - s * rtiles;
+            const int e = sexp[s];
+            const bool sh = e == E;
+            c_tiles = (sh ? static_cast<const uint8_t *>(p.Wsh_gu)
+                          : static_cast<const uint8_t *>(p.W_gu) + (size_t)e * 2 * I * H * esz) +
+                      (size_t)rt * nkt * 1024 + lane * 16;
+            if (WT == 1) {
+                const int sld = H / 128;
+                const float *sb = sh ? p.ssh_gu : p.s_gu + (size_t)e * (2 * I / 128) * sld;
+                c_srow = sb + (size_t)((g < 2 ? 8 * rt : I + 8 * rt) / 128) * sld;
+            }
         }
+        const uint8_t *tiles = c_tiles;
+        const float *srow = c_srow;
         const int k0 = ((f % nb) * kGuWaves + w) * KU;
 #pragma unroll
         for (int u = 0; u < KU; ++u) {

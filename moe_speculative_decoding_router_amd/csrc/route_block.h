@@ -23,9 +23,18 @@
 
 namespace moe {
 
-constexpr int kRouteNJ = kMaxExperts / 64;  // logits per lane
+constexpr int kRouteNJ = kMaxExperts / 64;  // row entries per lane
+constexpr int kRankSlots = kMaxTopK + 1;    // k, or k + 1 when the bias needs l_(k+1)
 
 __device__ __forceinline__ float nan_to_ninf(float v) { return v != v ? -INFINITY : v; }
+
+// Order-preserving unsigned image of a non-NaN float: a < b <=> ord(a) <
+// ord(b), and -0 maps like +0 (the two compare equal as floats).
+__device__ __forceinline__ unsigned float_ord(float x) {
+    unsigned u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 // Row of E logits into registers, entry lane + 64 j in v[j]; entries past E
 // read -inf.  Every load is issued (clamped to the row) before any is used,
@@ -38,46 +47,118 @@ __device__ __forceinline__ void load_logits(const float *row, int E, float (&v)[
     for (int j = 0; j < kRouteNJ; ++j) v[j] = lane + 64 * j < E ? nan_to_ninf(v[j]) : -INFINITY;
 }
 
-// Wave-wide selection of the best untaken entry under (value desc, index
-// asc).  v[j] holds entry lane + 64 j; `taken` marks entries this lane has
-// given out.  NaN compares as -inf; with k <= E an untaken entry always wins
-// over the empty sentinel.
-__device__ __forceinline__ void wave_select(const float (&v)[kRouteNJ], unsigned &taken, int E, float &bv, int &bi) {
+// Marks the K best valid entries of a row held by the wave (entry lane + 64 j
+// in slot j < NJ; bit j of `valid` flags it) in the order (key desc, index
+// asc).  A radix search from the most significant key bit keeps the bucket
+// that holds the K-th best entry and counts the entries above it, and stops
+// as soon as the bucket holds exactly the number still missing; if all 32 bits
+// are spent, the bucket holds equal keys and the lowest indices are taken.
+// Every count is a ballot popcount, so the result is the same in all lanes
+// that share the row.  Requires K <= number of valid entries.  Returns bit j
+// set where slot j of this lane is selected.
+template <int NJ>
+__device__ __forceinline__ unsigned wave_topk_mask(const unsigned (&key)[kRouteNJ], unsigned valid, int K) {
     const int lane = threadIdx.x & 63;
-    bv = -INFINITY;
-    bi = INT_MAX;
+    int cand = 0;
 #pragma unroll
-    for (int j = 0; j < kRouteNJ; ++j) {
-        const int e = lane + 64 * j;
-        const float vj = v[j] != v[j] ? -INFINITY : v[j];
-        if (e < E && !((taken >> j) & 1u) && better(vj, e, bv, bi)) {
-            bv = vj;
-            bi = e;
+    for (int j = 0; j < NJ; ++j) cand += __popcll(__ballot((valid >> j) & 1u));
+    int need = K;
+    unsigned P = 0u, M = 0u;
+    for (int b = 31; b >= 0 && cand != need; --b) {
+        const unsigned MM = M | (1u << b), PM = P | (1u << b);
+        int c1 = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) c1 += __popcll(__ballot(((valid >> j) & 1u) && (key[j] & MM) == PM));
+        c1 = __builtin_amdgcn_readfirstlane(c1);
+        if (c1 >= need) {
+            P = PM;
+            cand = c1;
+        } else {
+            need -= c1;
+            cand -= c1;
         }
+        M = MM;
+        P = __builtin_amdgcn_readfirstlane(P);
+        M = __builtin_amdgcn_readfirstlane(M);
     }
-    wave_argmax(bv, bi);
-    if (bi != INT_MAX && (bi & 63) == lane) taken |= 1u << (bi >> 6);
+    const bool ties = cand != need;  // only once every bit is decided
+    const unsigned long long below = (1ull << lane) - 1ull;
+    unsigned sel = 0u;
+    int left = need;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const bool v = (valid >> j) & 1u;
+        const unsigned km = key[j] & M;
+        const bool eq = v && km == P;
+        const unsigned long long bal = __ballot(eq);
+        const bool s = (v && km > P) || (eq && (!ties || __popcll(bal & below) < left));
+        left -= __popcll(bal);
+        if (s) sel |= 1u << j;
+    }
+    return sel;
+}
+
+// One selected entry on its way to rank order.
+struct RankEntry {
+    unsigned key;
+    int idx;
+    float v;   // value the weights are computed from
+    float v2;  // second carried value (original logit under the bias)
+};
+
+// Puts the K (<= kRankSlots) entries flagged by `sel` into rank order:
+// lane r < K receives the entry of rank r under (key desc, index asc).  buf is
+// this wave's 2 * kRankSlots entries of LDS.
+template <int NJ>
+__device__ __forceinline__ RankEntry wave_rank(unsigned sel, const unsigned (&key)[kRouteNJ], const float (&v)[kRouteNJ],
+                                               const float (&v2)[kRouteNJ], int K, RankEntry *buf) {
+    const int lane = threadIdx.x & 63;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const bool s = (sel >> j) & 1u;
+        const unsigned long long bal = __ballot(s);
+        if (s) buf[base + __popcll(bal & below)] = RankEntry{key[j], lane + 64 * j, v[j], v2[j]};
+        base += __popcll(bal);
+    }
+    if (lane < K) {
+        const RankEntry me = buf[lane];
+        int rank = 0;
+        for (int q = 0; q < K; ++q) {
+            const RankEntry o = buf[q];
+            rank += (o.key > me.key || (o.key == me.key && o.idx < me.idx)) ? 1 : 0;
+        }
+        buf[kRankSlots + rank] = me;
+    }
+    RankEntry out{0u, 0, -INFINITY, -INFINITY};
+    if (lane < K) out = buf[kRankSlots + lane];
+    return out;
 }
 
 // LDS scratch of block_route, carved from a byte buffer for runtime T, k, E.
 struct RouteScratch {
-    int *sel_i;                 // [T * k] first-pass selection (bias only)
-    float *cg;                  // [T * k] w_b * softmax(l_b)_e of the selected e
-    float *lam;                 // [T]
-    int *fin_i;                 // [T * k] final selection
-    float *fin_w;               // [T * k]
+    RankEntry *rank;            // [waves * 2 * kRankSlots]
     unsigned long long *tmask;  // [E] tokens routed to each expert
     unsigned long long *tmask0; // [E] first-pass membership (bias only)
+    int *sel_i;                 // [T * k] first-pass selection (bias only)
+    float *cg;                  // [T * k] w_b * softmax(l_b)_e of the selected e
+    int *fin_i;                 // [T * k] final selection
+    float *fin_w;               // [T * k]
     float *g;                   // [E]
     int *inP;                   // [E]
+    float *lam;                 // [T]
     int *wtot;                  // [2 * waves]
     int *misc;                  // [4]: U, |P*|
 
     __host__ __device__ static size_t bytes(int T, int k, int E, int waves) {
-        return (size_t)E * 16 + (size_t)T * k * 16 + (size_t)E * 8 + (size_t)T * 4 + (size_t)(2 * waves + 4) * 4 + 64;
+        return (size_t)waves * 2 * kRankSlots * sizeof(RankEntry) + (size_t)E * 16 + (size_t)T * k * 16 +
+               (size_t)E * 8 + (size_t)T * 4 + (size_t)(2 * waves + 4) * 4 + 64;
     }
     __device__ void carve(unsigned char *base, int T, int k, int E, int waves) {
         unsigned char *q = base;
+        rank = reinterpret_cast<RankEntry *>(q);
+        q += (size_t)waves * 2 * kRankSlots * sizeof(RankEntry);
         tmask = reinterpret_cast<unsigned long long *>(q);
         q += (size_t)E * 8;
         tmask0 = reinterpret_cast<unsigned long long *>(q);
@@ -105,11 +186,16 @@ struct RouteScratch {
 // Routes the call with NTHREADS threads (NTHREADS >= E).  Results:
 //   LDS: sexp[s] expert of slot s (E = shared expert), tw[s * T + t] gate
 //        weight of token t in slot s (0 if not routed), *nslots_lds.
-//   global (when write_global): topk_idx, topk_w, union, CSR, P*, meta, the
-//        slot tables (slot_expert, tokw, tokpos, tpos) of the FFN kernels.
-template <int NTHREADS>
-__device__ __forceinline__ void block_route(const VerifyParams &p, unsigned char *scratch, int *sexp, float *tw, int *nslots_lds,
-                            bool write_global) {
+//   global (when write_global): topk_idx, topk_w, union, CSR, P* (ascending),
+//        meta, the slot tables (slot_expert, tokw, tokpos, tpos) of the FFN
+//        kernels.
+// The first pass gives token t to wave t % (NTHREADS / 64); waves without a
+// token go straight to the first barrier (the caller may hand them other
+// work before the call).
+// NJ: row entries per lane the selections scan (>= ceil(E / 64)).
+template <int NTHREADS, int NJ>
+__device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned char *scratch, int *sexp, float *tw,
+                                               int *nslots_lds, bool write_global) {
     static_assert(NTHREADS >= kMaxExperts, "the union scan gives every expert one thread");
     constexpr int NW = NTHREADS / 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -117,41 +203,38 @@ __device__ __forceinline__ void block_route(const VerifyParams &p, unsigned char
     const bool bias = p.bias_on != 0;
     RouteScratch sh;
     sh.carve(scratch, T, k, E, NW);
+    RankEntry *rbuf = sh.rank + (size_t)w * 2 * kRankSlots;
+    unsigned valid = 0u;  // slots of this lane inside the row
+#pragma unroll
+    for (int j = 0; j < kRouteNJ; ++j)
+        if (lane + 64 * j < E) valid |= 1u << j;
 
+    // zeroing needs no barrier of its own: the first pass does not touch it
     for (int e = tid; e < E; e += NTHREADS) {
         sh.tmask[e] = 0ull;
         sh.tmask0[e] = 0ull;
         sh.inP[e] = 0;
     }
-    lds_barrier();
 
     // ---- pass 1: top-k (k + 1 when the bias needs the (k+1)-th logit);
-    //      lane r keeps the r-th choice in registers ----
+    //      lane r ends with the entry of rank r ----
     const int R = (bias && k < E) ? k + 1 : k;
     for (int t = w; t < T; t += NW) {
         float v[kRouteNJ];
+        unsigned key[kRouteNJ];
         load_logits(p.logits + (size_t)t * E, E, v);
         const float wc = bias ? p.w_conf[t] : 0.f;
-        unsigned taken = 0;
-        float m = 0.f, vk1 = 0.f, my_v = -INFINITY;
-        int my_i = 0;
-        for (int r = 0; r < R; ++r) {
-            float bv;
-            int bi;
-            wave_select(v, taken, E, bv, bi);
-            if (r == 0) m = bv;
-            if (r == k) vk1 = bv;
-            if (lane == r) {
-                my_v = bv;
-                my_i = bi;
-            }
-        }
+#pragma unroll
+        for (int j = 0; j < kRouteNJ; ++j) key[j] = float_ord(v[j]);
+        const unsigned sel = wave_topk_mask<NJ>(key, valid, R);
+        const RankEntry me = wave_rank<NJ>(sel, key, v, v, R, rbuf);
+        const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(me.v), 0));
         const bool mine = lane < k;
         if (!bias) {
-            const float ex = mine ? expf(my_v - m) : 0.f;
+            const float ex = mine ? expf(me.v - m) : 0.f;
             const float s = wave_sum(ex);
             if (mine) {
-                sh.fin_i[t * k + lane] = my_i;
+                sh.fin_i[t * k + lane] = me.idx;
                 sh.fin_w[t * k + lane] = ex / s;
             }
         } else {
@@ -162,18 +245,28 @@ __device__ __forceinline__ void block_route(const VerifyParams &p, unsigned char
                 if (lane + 64 * j < E) z += expf(v[j] - m);
             z = wave_sum(z);
             if (mine) {
-                sh.sel_i[t * k + lane] = my_i;
-                sh.cg[t * k + lane] = wc * (expf(my_v - m) / z);
-                if (my_i >= 0 && my_i < E) atomicOr(&sh.tmask0[my_i], 1ull << t);
+                sh.sel_i[t * k + lane] = me.idx;
+                sh.cg[t * k + lane] = wc * (expf(me.v - m) / z);
             }
             // lambda_b = alpha * (l_(1) - l_(k+1)), float32, no contraction (R6)
-            if (lane == 0) sh.lam[t] = k < E ? __fmul_rn(p.alpha, __fsub_rn(m, vk1)) : 0.f;
+            if (k < E) {
+                const float vk1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(me.v), k));
+                if (lane == 0) sh.lam[t] = __fmul_rn(p.alpha, __fsub_rn(m, vk1));
+            } else if (lane == 0) {
+                sh.lam[t] = 0.f;
+            }
         }
     }
     lds_barrier();
 
     if (bias) {
-        // ---- importance g_e (R4), summed in token order ----
+        // ---- first-pass membership, then importance g_e (R4) summed in
+        //      token order ----
+        for (int i = tid; i < T * k; i += NTHREADS) {
+            const int e = sh.sel_i[i];
+            if (e >= 0 && e < E) atomicOr(&sh.tmask0[e], 1ull << (i / k));
+        }
+        lds_barrier();
         for (int e = tid; e < E; e += NTHREADS) {
             float g = 0.f;
             const unsigned long long m0 = sh.tmask0[e];
@@ -184,24 +277,35 @@ __device__ __forceinline__ void block_route(const VerifyParams &p, unsigned char
             sh.g[e] = g;
         }
         lds_barrier();
-        // ---- preferred set P*: top-cap by (g desc, index asc), g > 0 (R5) ----
+        // ---- preferred set P*: top-cap by (g desc, index asc) among g > 0 (R5) ----
         if (w == 0) {
-            float gv[kRouteNJ];
+            unsigned key[kRouteNJ];
+            unsigned pos = 0u;
 #pragma unroll
             for (int j = 0; j < kRouteNJ; ++j) {
                 const int e = lane + 64 * j;
-                gv[j] = e < E ? sh.g[e] : -INFINITY;
+                const float g = e < E ? sh.g[e] : 0.f;
+                key[j] = float_ord(g);
+                if (e < E && g > 0.f) pos |= 1u << j;
             }
-            unsigned taken = 0;
-            int n = 0;
-            for (; n < p.cap; ++n) {
-                float bv;
-                int bi;
-                wave_select(gv, taken, E, bv, bi);
-                if (bi < 0 || bi >= E || !(bv > 0.f)) break;
-                if (lane == 0) {
-                    sh.inP[bi] = 1;
-                    if (write_global) p.pstar[n] = bi;
+            int npos = 0;
+#pragma unroll
+            for (int j = 0; j < kRouteNJ; ++j)
+                if (j < NJ) npos += __popcll(__ballot((pos >> j) & 1u));
+            const int n = min(p.cap, npos);
+            const unsigned sel = wave_topk_mask<NJ>(key, pos, n);
+            const unsigned long long below = (1ull << lane) - 1ull;
+            int base = 0;
+#pragma unroll
+            for (int j = 0; j < kRouteNJ; ++j) {
+                if (j < NJ) {
+                    const bool s = (sel >> j) & 1u;
+                    const unsigned long long bal = __ballot(s);
+                    if (s) {
+                        sh.inP[lane + 64 * j] = 1;
+                        if (write_global) p.pstar[base + __popcll(bal & below)] = lane + 64 * j;
+                    }
+                    base += __popcll(bal);
                 }
             }
             if (lane == 0) sh.misc[1] = n;
@@ -210,36 +314,23 @@ __device__ __forceinline__ void block_route(const VerifyParams &p, unsigned char
         // ---- re-select on the biased logits; weights from the original (R6, R7) ----
         for (int t = w; t < T; t += NW) {
             float v[kRouteNJ], vb[kRouteNJ];
+            unsigned key[kRouteNJ];
             load_logits(p.logits + (size_t)t * E, E, v);
             const float lam = sh.lam[t];
 #pragma unroll
             for (int j = 0; j < kRouteNJ; ++j) {
                 const int e = lane + 64 * j;
                 vb[j] = (e < E && sh.inP[e]) ? __fadd_rn(v[j], lam) : v[j];
+                key[j] = float_ord(vb[j]);
             }
-            unsigned taken = 0;
-            float my_ov = -INFINITY;
-            int my_i = 0;
-            for (int r = 0; r < k; ++r) {
-                float bv;
-                int bi;
-                wave_select(vb, taken, E, bv, bi);
-                float ov = -INFINITY;  // original logit of the chosen expert
-#pragma unroll
-                for (int j = 0; j < kRouteNJ; ++j)
-                    if (lane + 64 * j == bi) ov = v[j];
-                ov = wave_max(ov);
-                if (lane == r) {
-                    my_ov = ov;
-                    my_i = bi;
-                }
-            }
+            const unsigned sel = wave_topk_mask<NJ>(key, valid, k);
+            const RankEntry me = wave_rank<NJ>(sel, key, vb, v, k, rbuf);
             const bool mine = lane < k;
-            const float m = wave_max(mine ? my_ov : -INFINITY);
-            const float ex = mine ? expf(my_ov - m) : 0.f;
+            const float m = wave_max(mine ? me.v2 : -INFINITY);
+            const float ex = mine ? expf(me.v2 - m) : 0.f;
             const float s = wave_sum(ex);
             if (mine) {
-                sh.fin_i[t * k + lane] = my_i;
+                sh.fin_i[t * k + lane] = me.idx;
                 sh.fin_w[t * k + lane] = ex / s;
             }
         }
@@ -347,6 +438,18 @@ __device__ __forceinline__ void block_route(const VerifyParams &p, unsigned char
         }
     }
     lds_barrier();
+}
+
+// Routing with the selection loops sized for E.
+template <int NTHREADS>
+__device__ __forceinline__ void block_route(const VerifyParams &p, unsigned char *scratch, int *sexp, float *tw,
+                                            int *nslots_lds, bool write_global) {
+    if (p.E <= 128)
+        block_route_nj<NTHREADS, 2>(p, scratch, sexp, tw, nslots_lds, write_global);
+    else if (p.E <= 256)
+        block_route_nj<NTHREADS, 4>(p, scratch, sexp, tw, nslots_lds, write_global);
+    else
+        block_route_nj<NTHREADS, kRouteNJ>(p, scratch, sexp, tw, nslots_lds, write_global);
 }
 
 }  // namespace moe
