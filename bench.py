@@ -48,7 +48,6 @@ def parse():
     ap.add_argument("--bias", action="store_true", help="turn the reuse-aware soft bias on")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-profile-pass", action="store_true")
     return ap.parse_args()
 
 
@@ -95,11 +94,11 @@ def main() -> int:
 
     ML = args.model_layers or MODEL_LAYERS[wl.name]
 
-    def step(i, events=None):
+    def step(i):
         m.select_drafts(trees.parent, P_d, F_d, 4, out=S_d)
         for j in range(ML):
             lw, x = layers[(i * ML + j) % L]
-            m.verify_layer(x, lw, bias, out=y, workspace=wsp, events=events[j] if events else None)
+            m.verify_layer(x, lw, bias, out=y, workspace=wsp)
 
     # union size per layer -> unique-expert bytes
     be = m.expert_bytes(wl.H, wl.I, wl.wdtype)
@@ -116,13 +115,34 @@ def main() -> int:
     err(f"[bench] unions per layer: {U}")
 
     # ---------------- timed region ----------------
+    # Every EV_STRIDE-th verify call of the region (the stride is coprime with
+    # the cycled layer count, so every layer is sampled) carries a start/end
+    # event pair per stage, recorded by the kernel launches themselves on the
+    # stream the kernels run on; the per-kernel durations come from the same
+    # region as the headline value.  (Event pairs on every call would add
+    # about 30 us of packet gaps per call.)
+    calls = [(i, j) for i in range(args.steps) for j in range(ML)]
+    EV_STRIDE = 31 if len(calls) >= 4 * 31 else 1   # short runs: every call
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    NS = m.NUM_STAGES
+    sampled = [c for n, c in enumerate(calls) if n % EV_STRIDE == EV_STRIDE // 2]
+    evs = {c: [torch.cuda.Event(enable_timing=True) for _ in range(2 * NS)] for c in sampled}
+    for e in (e for row in evs.values() for e in row):   # torch creates the HIP event at its first record
+        e.record(stream)
+    torch.cuda.synchronize()
+
+    def timed_step(i):
+        m.select_drafts(trees.parent, P_d, F_d, 4, out=S_d)
+        for j in range(ML):
+            lw, x = layers[(i * ML + j) % L]
+            m.verify_layer(x, lw, bias, out=y, workspace=wsp, events=evs.get((i, j)))
+
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(args.steps):
-        step(i)
+        timed_step(i)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
@@ -131,38 +151,22 @@ def main() -> int:
     value = total_bytes / (total_ms * 1e-3) / 1e9
     err(f"[bench] {args.steps} steps x {ML} layers in {total_ms:.3f} ms -> {ms_step * 1e3:.1f} us/step, "
         f"{ms_step * 1e3 / ML:.1f} us/layer, {value:.0f} GB/s")
-
-    # ---------------- per-kernel profile region (events between stages) ----------------
-    # The same steps again with HIP events recorded on the stream between the
-    # stages of every verify call (the events add a little time of their own).
-    stage_ms = None
-    if not args.no_profile_pass:
-        PS = min(args.steps, 4)
-        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(m.NUM_STAGES + 1)] for _ in range(ML)]
-               for _ in range(PS)]
-        sel0 = [torch.cuda.Event(enable_timing=True) for _ in range(PS)]
-        for e in [e for st in evs for row in st for e in row] + sel0:   # torch creates the HIP event at first record
-            e.record(stream)
-        torch.cuda.synchronize()
-        for i in range(PS):
-            sel0[i].record(stream)
-            step(i, events=evs[i])
-        torch.cuda.synchronize()
-        stage_ms = np.array([[evs[i][j][q].elapsed_time(evs[i][j][q + 1]) for q in range(m.NUM_STAGES)]
-                             for i in range(PS) for j in range(ML)])
-        sel_ms = np.array([sel0[i].elapsed_time(evs[i][0][0]) for i in range(PS)])
-        layer_ms = stage_ms.sum(axis=1)
-        lidx = [(i * ML + j) % L for i in range(PS) for j in range(ML)]
-        step_bytes = np.array([bytes_layer[q] for q in lidx], dtype=np.float64)
-        gu_bytes = np.array([(U[q] + n_sh) * gu_bytes_e for q in lidx], dtype=np.float64)
-        d_bytes = np.array([(U[q] + n_sh) * d_bytes_e for q in lidx], dtype=np.float64)
+    # kernel durations [sampled calls, stages] in ms
+    stage_ms = np.array([[evs[c][2 * q].elapsed_time(evs[c][2 * q + 1]) for q in range(NS)] for c in sampled])
+    lidx = [(i * ML + j) % L for (i, j) in sampled]
+    kbytes = {  # algorithmic bytes per launch of each kernel
+        "router": np.array([wl.E * wl.H * 4 + T * wl.H * 4 + T * wl.E * 4 for _ in lidx], dtype=np.float64),
+        "gate_up": np.array([(U[q] + n_sh) * gu_bytes_e for q in lidx], dtype=np.float64),
+        "down": np.array([(U[q] + n_sh) * d_bytes_e for q in lidx], dtype=np.float64),
+    }
+    ffn_ms = stage_ms[:, 2] + stage_ms[:, 3]
+    ffn_bytes = kbytes["gate_up"] + kbytes["down"]
 
     # ---------------- CPU oracle baseline (bounded sample) ----------------
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds, U[0], be, n_sh)
 
-    us_layer = float(layer_ms.mean() * 1e3) if stage_ms is not None else None
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -185,27 +189,66 @@ def main() -> int:
         "us_per_step": round(ms_step * 1e3, 2),
         "verify_us_per_layer_incl_select": round(ms_step * 1e3 / ML, 2),
     }
-    if stage_ms is not None:
-        gu_ms = stage_ms[:, 2]
-        d_ms = stage_ms[:, 3]
-        ffn_ms = gu_ms + d_ms
-        out["verify_us_per_layer_profiled"] = round(us_layer, 2)
-        out["verify_GBs"] = round(float(step_bytes.sum() / (layer_ms.sum() * 1e-3) / 1e9), 1)
-        out["ffn_GBs"] = round(float(step_bytes.sum() / (ffn_ms.sum() * 1e-3) / 1e9), 1)
-        out["stages_us"] = {name: round(float(stage_ms[:, j].mean() * 1e3), 2)
-                            for j, name in enumerate(m.STAGE_NAMES)}
-        out["stages_us"]["select_drafts"] = round(float(sel_ms.mean() * 1e3), 2)
-        ach = float(gu_bytes.mean() / (gu_ms.mean() * 1e-3) / 1e9)
-        out["roofline"] = {"kernel": "ffn gate_up (ffn_mfma_kernel, gate-up instance)", "bound": "hbm",
-                           "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                           "bytes_per_launch": round(float(gu_bytes.mean())), "avg_us": round(float(gu_ms.mean() * 1e3), 2)}
-        out["roofline_down"] = {"achieved": round(float(d_bytes.mean() / (d_ms.mean() * 1e-3) / 1e9), 1),
-                                "avg_us": round(float(d_ms.mean() * 1e3), 2)}
+    # the kernels every bf16/fp8 call runs (the route stage runs a kernel only
+    # when the routing scratch exceeds LDS; combine only for float32 weights)
+    kernels = {}
+    for q, name in enumerate(m.STAGE_NAMES):
+        if name not in kbytes:
+            continue
+        kernels[name] = {"avg_us": round(float(stage_ms[:, q].mean() * 1e3), 2), "launches": len(lidx),
+                         "bytes_per_launch": round(float(kbytes[name].mean())),
+                         "GBs": round(float(kbytes[name].sum() / (stage_ms[:, q].sum() * 1e-3) / 1e9), 1)}
+    out["kernels"] = kernels
+    out["kernel_events"] = f"start/end events on 1 in {EV_STRIDE} verify calls of the timed region ({len(sampled)} calls)"
+    out["ffn_us_per_layer"] = round(float(ffn_ms.mean() * 1e3), 2)
+    out["ffn_GBs"] = round(float(ffn_bytes.sum() / (ffn_ms.sum() * 1e-3) / 1e9), 1)
+    out["ffn_frac_of_hbm_peak"] = round(out["ffn_GBs"] / HBM_PEAK_GBS, 4)
+    gu = kernels["gate_up"]
+    out["roofline"] = {"kernel": "gateup_kernel (router top-k + union + gate/up SwiGLU over the union experts)",
+                       "bound": "hbm", "achieved": gu["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gu["GBs"] / HBM_PEAK_GBS, 4),
+                       "traffic": measured_traffic(wl.name, "gate_up"),
+                       "bytes_per_launch": gu["bytes_per_launch"], "avg_us": gu["avg_us"]}
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0
+
+
+KERNEL_SOURCES = ("ffn.hip", "route_block.h", "common.h", "internal.h")
+
+
+def kernel_source_digest():
+    """sha256 over the sources the FFN kernels are compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "moe_speculative_decoding_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary of
+    this workload (FETCH_SIZE and WRITE_SIZE scaled by the pack kernel, a
+    plain permutation copy of known size, in the same runs), or None when the
+    summary is missing or the kernel source changed since the counters were
+    taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.md")
+    try:
+        lines = open(path).read().splitlines()
+        digest = kernel_source_digest()
+    except OSError:
+        return None
+    kv = {}
+    for ln in lines:
+        if ln.startswith("- ") and ": " in ln:
+            key, val = ln[2:].split(": ", 1)
+            kv[key.strip("` ")] = val.strip("` ")
+    if kv.get("kernel source sha256") != digest:
+        return None
+    v = kv.get(f"{kernel} HBM bytes per launch")
+    return int(float(v)) if v else None
 
 
 def cpu_baseline(wl, budget_s, U0, be, n_sh):

@@ -102,9 +102,13 @@ typedef struct {
  *   csr_tok [T * k] i32        tokens of each union expert, ascending
  *   csr_w [T * k] f32          gate weight of each (expert, token) entry
  *   pstar [E] i32, pstar_size [1] i32   preferred set P* (bias only)
- *   events: NULL or (host) array of MOE_NUM_STAGES + 1 hipEvent_t handles
- *           created by the caller; event i is recorded on `stream` before
- *           stage i and event MOE_NUM_STAGES after the last stage. */
+ *   events: NULL or (host) array of 2 * MOE_NUM_STAGES hipEvent_t handles
+ *           created by the caller with timing enabled.  Events 2i and 2i + 1
+ *           mark the start and the end of the execution of stage i's kernel
+ *           on `stream` (the kernel is launched with hipExtLaunchKernelGGL);
+ *           a stage that runs no kernel in this call (the route stage when
+ *           the gate-up kernel routes, the combine stage for bf16/fp8)
+ *           records both at that point of the stream. */
 typedef struct {
     float *logits;
     int32_t *topk_idx;

@@ -245,8 +245,10 @@ def verify_layer(x, layer: LayerWeights, bias: Optional[Bias] = None, *, out=Non
     a = workspace.aux
     ev_arr = None
     if events is not None:
-        ev_arr = (ctypes.c_void_p * (NUM_STAGES + 1))(*[int(e.cuda_event) if hasattr(e, "cuda_event") else int(e)
-                                                         for e in events])
+        if len(events) != 2 * NUM_STAGES:
+            raise ValueError(f"events: need {2 * NUM_STAGES} events (start, end of each stage)")
+        ev_arr = (ctypes.c_void_p * (2 * NUM_STAGES))(*[int(e.cuda_event) if hasattr(e, "cuda_event") else int(e)
+                                                        for e in events])
     caux = _Aux(*([_ptr(getattr(a, f)) for f in Aux.__dataclass_fields__] if a else [None] * 10),
                 ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
     s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream

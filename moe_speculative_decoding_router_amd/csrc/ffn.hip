@@ -626,49 +626,47 @@ GuPlan plan_gateup(const VerifyParams &p) {
 }
 
 template <typename K>
-hipError_t launch_gu(K kernel, const VerifyParams &p, size_t dyn, int n_cu, hipStream_t s) {
+hipError_t launch_gu(K kernel, const VerifyParams &p, size_t dyn, int n_cu, hipStream_t s, KernelEvents ev) {
     if (dyn > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)dyn) != hipSuccess)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kernel, dim3(n_cu * kGateUpWgPerCu), dim3(kGuWaves * 64), dyn, s, p);
-    return hipGetLastError();
+    return launch_k(kernel, dim3(n_cu * kGateUpWgPerCu), dim3(kGuWaves * 64), dyn, s, ev, p);
 }
 
 template <int WT, int NT, bool SPLIT, bool GU>
-hipError_t launch_one(const VerifyParams &p, int n_cu, hipStream_t s) {
+hipError_t launch_one(const VerifyParams &p, int n_cu, hipStream_t s, KernelEvents ev) {
     if (GU) {
         const GuPlan pl = plan_gateup(p);
         VerifyParams q = p;
         q.gu_async_x = pl.async_x ? 1 : 0;
-        if (pl.fused && pl.blds) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true>, q, pl.dyn, n_cu, s);
-        if (pl.fused) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, false>, q, pl.dyn, n_cu, s);
-        return launch_gu(gateup_kernel<WT, NT, SPLIT, false, false>, q, 0, n_cu, s);
+        if (pl.fused && pl.blds) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true>, q, pl.dyn, n_cu, s, ev);
+        if (pl.fused) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, false>, q, pl.dyn, n_cu, s, ev);
+        return launch_gu(gateup_kernel<WT, NT, SPLIT, false, false>, q, 0, n_cu, s, ev);
     } else {
         auto kernel = down_kernel<WT, NT, SPLIT>;
         static const int cap = resident_grid(kernel, kDnWaves * 64, n_cu, kDownWgPerCu, 0);
         const int rtiles = p.H / 16;  // one workgroup per row tile when they all fit at once
-        hipLaunchKernelGGL(kernel, dim3(rtiles < cap ? rtiles : cap), dim3(kDnWaves * 64), 0, s, p);
+        return launch_k(kernel, dim3(rtiles < cap ? rtiles : cap), dim3(kDnWaves * 64), 0, s, ev, p);
     }
-    return hipGetLastError();
 }
 
 template <int WT, bool GU>
-hipError_t launch_mfma(const VerifyParams &p, int n_cu, hipStream_t s) {
+hipError_t launch_mfma(const VerifyParams &p, int n_cu, hipStream_t s, KernelEvents ev) {
     const int nt = (p.cols + 15) / 16;
     if (p.split) {
         switch (nt) {
-            case 1: return launch_one<WT, 1, true, GU>(p, n_cu, s);
-            case 2: return launch_one<WT, 2, true, GU>(p, n_cu, s);
-            case 3: return launch_one<WT, 3, true, GU>(p, n_cu, s);
-            default: return launch_one<WT, 4, true, GU>(p, n_cu, s);
+            case 1: return launch_one<WT, 1, true, GU>(p, n_cu, s, ev);
+            case 2: return launch_one<WT, 2, true, GU>(p, n_cu, s, ev);
+            case 3: return launch_one<WT, 3, true, GU>(p, n_cu, s, ev);
+            default: return launch_one<WT, 4, true, GU>(p, n_cu, s, ev);
         }
     }
     switch (nt) {
-        case 1: return launch_one<WT, 1, false, GU>(p, n_cu, s);
-        case 2: return launch_one<WT, 2, false, GU>(p, n_cu, s);
-        case 3: return launch_one<WT, 3, false, GU>(p, n_cu, s);
-        default: return launch_one<WT, 4, false, GU>(p, n_cu, s);
+        case 1: return launch_one<WT, 1, false, GU>(p, n_cu, s, ev);
+        case 2: return launch_one<WT, 2, false, GU>(p, n_cu, s, ev);
+        case 3: return launch_one<WT, 3, false, GU>(p, n_cu, s, ev);
+        default: return launch_one<WT, 4, false, GU>(p, n_cu, s, ev);
     }
 }
 
@@ -676,30 +674,23 @@ hipError_t launch_mfma(const VerifyParams &p, int n_cu, hipStream_t s) {
 
 bool gateup_fuses_routing(const VerifyParams &p) { return p.wdtype != 0 && plan_gateup(p).fused; }
 
-hipError_t launch_gateup(const VerifyParams &p, int n_cu, hipStream_t s) {
+hipError_t launch_gateup(const VerifyParams &p, int n_cu, hipStream_t s, KernelEvents ev) {
     const int grid = n_cu * 4;
-    if (p.wdtype == 0) {
-        hipLaunchKernelGGL(gateup_f32_kernel, dim3(grid), dim3(kFfnThreads), 0, s, p);
-        return hipGetLastError();
-    }
-    return p.wdtype == 1 ? launch_mfma<0, true>(p, n_cu, s) : launch_mfma<1, true>(p, n_cu, s);
+    if (p.wdtype == 0) return launch_k(gateup_f32_kernel, dim3(grid), dim3(kFfnThreads), 0, s, ev, p);
+    return p.wdtype == 1 ? launch_mfma<0, true>(p, n_cu, s, ev) : launch_mfma<1, true>(p, n_cu, s, ev);
 }
 
-hipError_t launch_down(const VerifyParams &p, int n_cu, hipStream_t s) {
+hipError_t launch_down(const VerifyParams &p, int n_cu, hipStream_t s, KernelEvents ev) {
     const int grid = n_cu * 4;
-    if (p.wdtype == 0) {
-        hipLaunchKernelGGL(down_f32_kernel, dim3(grid), dim3(kFfnThreads), 0, s, p);
-        return hipGetLastError();
-    }
-    return p.wdtype == 1 ? launch_mfma<0, false>(p, n_cu, s) : launch_mfma<1, false>(p, n_cu, s);
+    if (p.wdtype == 0) return launch_k(down_f32_kernel, dim3(grid), dim3(kFfnThreads), 0, s, ev, p);
+    return p.wdtype == 1 ? launch_mfma<0, false>(p, n_cu, s, ev) : launch_mfma<1, false>(p, n_cu, s, ev);
 }
 
-hipError_t launch_combine(const VerifyParams &p, hipStream_t s) {
+hipError_t launch_combine(const VerifyParams &p, hipStream_t s, KernelEvents ev) {
     if (p.wdtype != 0) return hipSuccess;  // the matrix-core down kernel writes y itself
     int blocks = (p.T * p.H + 255) / 256;
     if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, p);
-    return hipGetLastError();
+    return launch_k(combine_kernel, dim3(blocks), dim3(256), 0, s, ev, p);
 }
 
 }  // namespace moe

@@ -1,6 +1,7 @@
 // Internal declarations shared by the HIP translation units of libmoeverify.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,12 +49,28 @@ struct VerifyParams {
 constexpr int kWaveSize = 64;
 
 // Launchers (enqueue only; return hipError_t of the launch).
-hipError_t launch_router(const VerifyParams &p, hipStream_t s);
-hipError_t launch_route(const VerifyParams &p, hipStream_t s);
-hipError_t launch_gateup(const VerifyParams &p, int n_cu, hipStream_t s);
+// Optional timing of one launch: with both events set, the kernel is
+// launched through hipExtLaunchKernelGGL so that the events mark the start
+// and the end of its execution on the stream.
+struct KernelEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename F, typename... Args>
+hipError_t launch_k(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, KernelEvents ev, Args... args) {
+    if (ev.start && ev.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    return hipGetLastError();
+}
+
+hipError_t launch_router(const VerifyParams &p, hipStream_t s, KernelEvents ev = {});
+hipError_t launch_route(const VerifyParams &p, hipStream_t s, KernelEvents ev = {});
+hipError_t launch_gateup(const VerifyParams &p, int n_cu, hipStream_t s, KernelEvents ev = {});
 bool gateup_fuses_routing(const VerifyParams &p);  // routing runs in the gate-up prologue
-hipError_t launch_down(const VerifyParams &p, int n_cu, hipStream_t s);
-hipError_t launch_combine(const VerifyParams &p, hipStream_t s);
+hipError_t launch_down(const VerifyParams &p, int n_cu, hipStream_t s, KernelEvents ev = {});
+hipError_t launch_combine(const VerifyParams &p, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_pack(const void *src, void *dst, int E, int R, int K, int esz, int interleave, int half,
                        hipStream_t s);
 hipError_t launch_union_stats(const int32_t *topk_idx, int nL, int T, int k, int E, int32_t *counts,

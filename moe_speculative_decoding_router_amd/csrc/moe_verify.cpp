@@ -204,23 +204,30 @@ int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const mo
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int ncu = cu_count();
-    hipEvent_t ev[MOE_NUM_STAGES + 1] = {};
+    moe::KernelEvents kev[MOE_NUM_STAGES];
     if (a.events)
-        for (int i = 0; i <= MOE_NUM_STAGES; ++i) ev[i] = static_cast<hipEvent_t>(a.events[i]);
-    auto mark = [&](int i) -> bool { return !a.events || hipEventRecord(ev[i], s) == hipSuccess; };
+        for (int i = 0; i < MOE_NUM_STAGES; ++i)
+            kev[i] = {static_cast<hipEvent_t>(a.events[2 * i]), static_cast<hipEvent_t>(a.events[2 * i + 1])};
+    // a stage without a kernel in this call records its two events back to back
+    auto no_kernel = [&](int i) -> bool {
+        return !a.events ||
+               (hipEventRecord(kev[i].start, s) == hipSuccess && hipEventRecord(kev[i].stop, s) == hipSuccess);
+    };
 
     hipError_t err = hipSuccess;
-    if (!mark(0)) return fail(MOE_EHIP, "hipEventRecord failed");
-    if ((err = moe::launch_router(p, s)) != hipSuccess) goto hip_fail;
-    if (!mark(1)) return fail(MOE_EHIP, "hipEventRecord failed");
-    if (!moe::gateup_fuses_routing(p) && (err = moe::launch_route(p, s)) != hipSuccess) goto hip_fail;
-    if (!mark(2)) return fail(MOE_EHIP, "hipEventRecord failed");
-    if ((err = moe::launch_gateup(p, ncu, s)) != hipSuccess) goto hip_fail;
-    if (!mark(3)) return fail(MOE_EHIP, "hipEventRecord failed");
-    if ((err = moe::launch_down(p, ncu, s)) != hipSuccess) goto hip_fail;
-    if (!mark(4)) return fail(MOE_EHIP, "hipEventRecord failed");
-    if ((err = moe::launch_combine(p, s)) != hipSuccess) goto hip_fail;
-    if (!mark(5)) return fail(MOE_EHIP, "hipEventRecord failed");
+    if ((err = moe::launch_router(p, s, kev[0])) != hipSuccess) goto hip_fail;
+    if (!moe::gateup_fuses_routing(p)) {
+        if ((err = moe::launch_route(p, s, kev[1])) != hipSuccess) goto hip_fail;
+    } else if (!no_kernel(1)) {
+        return fail(MOE_EHIP, "hipEventRecord failed");
+    }
+    if ((err = moe::launch_gateup(p, ncu, s, kev[2])) != hipSuccess) goto hip_fail;
+    if ((err = moe::launch_down(p, ncu, s, kev[3])) != hipSuccess) goto hip_fail;
+    if (L.wdtype == MOE_F32) {
+        if ((err = moe::launch_combine(p, s, kev[4])) != hipSuccess) goto hip_fail;
+    } else if (!no_kernel(4)) {
+        return fail(MOE_EHIP, "hipEventRecord failed");
+    }
     return MOE_OK;
 hip_fail:
     return fail(MOE_EHIP, "kernel launch failed: %s", hipGetErrorString(err));

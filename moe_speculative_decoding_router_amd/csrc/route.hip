@@ -122,24 +122,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(VerifyParams p) {
 
 }  // namespace
 
-hipError_t launch_router(const VerifyParams &p, hipStream_t s) {
-    if (p.H % 4 == 0)
-        hipLaunchKernelGGL(router_kernel<true>, dim3(p.E), dim3(kRouterThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(router_kernel<false>, dim3(p.E), dim3(kRouterThreads), 0, s, p);
-    return hipGetLastError();
+hipError_t launch_router(const VerifyParams &p, hipStream_t s, KernelEvents ev) {
+    if (p.H % 4 == 0) return launch_k(router_kernel<true>, dim3(p.E), dim3(kRouterThreads), 0, s, ev, p);
+    return launch_k(router_kernel<false>, dim3(p.E), dim3(kRouterThreads), 0, s, ev, p);
 }
 
 size_t route_lds_bytes(const VerifyParams &p) { return RouteScratch::bytes(p.T, p.k, p.E, kRouteThreads / 64); }
 
-hipError_t launch_route(const VerifyParams &p, hipStream_t s) {
+hipError_t launch_route(const VerifyParams &p, hipStream_t s, KernelEvents ev) {
     const size_t lds = route_lds_bytes(p);
     if (lds > 64 * 1024 &&
         hipFuncSetAttribute(reinterpret_cast<const void *>(route_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds) != hipSuccess)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), lds, s, p);
-    return hipGetLastError();
+    return launch_k(route_kernel, dim3(1), dim3(kRouteThreads), lds, s, ev, p);
 }
 
 }  // namespace moe

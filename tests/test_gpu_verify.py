@@ -138,6 +138,42 @@ def test_deterministic_two_runs():
         assert np.array_equal(a[key], b[key]), key
 
 
+@pytest.mark.parametrize("wdtype", ["bf16", "f32"])
+def test_stage_events_bracket_the_kernels(wdtype):
+    """Per-stage start/end events: the kernels that run have positive
+    durations, a stage without a kernel spans only its two back-to-back event
+    records (a few microseconds), and timing does not change the result."""
+    log(f"case stage events ({wdtype})")
+    if wdtype == "bf16":
+        wl = small("qwen3_bf16", T=5, **SMALL_BF16)
+        x, _, Wr = synth.layer_inputs(wl, 0)
+        from gpu_helpers import device_layer
+        lw = device_layer(wl, 0, Wr)
+    else:
+        wl = synth.WORKLOADS["tiny_f32"]
+        x, Wr, Wgu, Wd = synth.tiny_f32_arrays(wl)
+        lw = f32_layer(Wr, Wgu, Wd, wl.k)
+    ref = run_layer(lw, x)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * m.NUM_STAGES)]
+    stream = torch.cuda.current_stream()
+    for e in evs:
+        e.record(stream)
+    torch.cuda.synchronize()
+    wsp = m.alloc_workspace(lw, x.shape[0])
+    y, _ = m.verify_layer(to_dev(x), lw, workspace=wsp, events=evs)
+    torch.cuda.synchronize()
+    ms = {name: evs[2 * i].elapsed_time(evs[2 * i + 1]) for i, name in enumerate(m.STAGE_NAMES)}
+    log(f"    stage ms {ms}")
+    assert ms["router"] > 0 and ms["gate_up"] > 0 and ms["down"] > 0
+    if wdtype == "bf16":
+        assert ms["combine"] < 0.02
+    else:
+        assert ms["combine"] > 0 and ms["route"] > 0
+    assert np.array_equal(y.cpu().numpy(), ref["y"])
+    with pytest.raises(ValueError):
+        m.verify_layer(to_dev(x), lw, workspace=wsp, events=evs[:-1])
+
+
 def test_workspace_error_through_real_library():
     wl = small("qwen3_bf16", T=5, **SMALL_BF16)
     x, _, Wr = synth.layer_inputs(wl, 0)
