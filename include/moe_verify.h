@@ -129,13 +129,16 @@ typedef struct {
  * overlap src).  gate_up = 1: src is the gate-up matrix, rows = 2I, K = H;
  * gate_up = 0: the down matrix, rows = H, K = I.
  * Layout of dst: per expert, 1 KB tiles of 16 rows x 32 k (bf16) or 16 rows x
- * 64 k (fp8), row-tile major then K-tile; inside a tile, 16-byte slot
- * l = 0..63 holds tile row l % 16 at k offset (l / 16) * 8 (bf16) or
- * (l / 16) * 16 (fp8), the operand order of v_mfma_f32_16x16x32_bf16, so a
- * wave reads 1 KB of contiguous memory per load.  For gate_up = 1, row tile rt
+ * 64 k (fp8); inside a tile, 16-byte slot l = 0..63 holds tile row l % 16 at
+ * k offset (l / 16) * 8 (bf16) or (l / 16) * 16 (fp8), the operand order of
+ * v_mfma_f32_16x16x32_bf16, so a wave reads 1 KB of contiguous memory per
+ * load.  gate_up = 1: tiles ordered row-tile major, then K-tile; row tile rt
  * holds gate rows 8 rt .. 8 rt + 7 as tile rows 0..7 and up rows
- * I + 8 rt .. I + 8 rt + 7 as tile rows 8..15.
- * Requires rows % 16 == 0 and K % 32 (bf16) / K % 64 (fp8) == 0. */
+ * I + 8 rt .. I + 8 rt + 7 as tile rows 8..15.  gate_up = 0: tiles ordered in
+ * groups of 4 row tiles (64 rows): group major, then K-tile, then the row
+ * tile inside the group (rows 16 (4 grp + r) .. + 15).
+ * Requires K % 32 (bf16) / K % 64 (fp8) == 0, rows % 32 == 0 for gate_up = 1
+ * and rows % 64 == 0 for gate_up = 0. */
 int moe_pack_weights(const void *src, void *dst, int32_t E, int32_t rows, int32_t K, int32_t wdtype,
                      int32_t gate_up, void *stream);
 
@@ -153,8 +156,8 @@ size_t moe_verify_workspace_bytes(const moe_layer *layer, int32_t T, const moe_b
  * layer (host), bias (host, NULL = off), aux (host, NULL = no extra outputs).
  * ws: device workspace of at least moe_verify_workspace_bytes() bytes,
  * 256-byte aligned; its contents need no initialisation and are clobbered.
- * Limits: 1 <= T <= 64, 1 <= k <= min(E, 32), E <= 512; bf16: H, I multiples
- * of 32; fp8: H, I multiples of 128.  Numerics: router GEMV and FFN
+ * Limits: 1 <= T <= 64, 1 <= k <= min(E, 32), E <= 512; bf16: H a multiple of
+ * 64 and I of 32; fp8: H, I multiples of 128.  Numerics: router GEMV and FFN
  * accumulate in float32; activations enter the bf16/fp8 matrix-core
  * products as a bf16 high/low pair when T <= 32 (as one bf16 otherwise). */
 int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const moe_bias *bias,

@@ -33,7 +33,6 @@ namespace {
 
 constexpr int kFfnThreads = 256;
 constexpr int kGateUpWgPerCu = 1;  // persistent workgroups per CU (8 waves each)
-constexpr int kDownWgPerCu = 2;  // capacity bound; the grid is one workgroup per row tile
 constexpr size_t kLdsPerCu = 160 * 1024;      // LDS of one gfx950 compute unit
 
 // 16 bytes per lane from global memory straight into LDS
@@ -261,29 +260,33 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     unsigned char *scr = dyn_lds + (async_x ? xb_bytes : 0);
     float *tw_lds = reinterpret_cast<float *>(
         dyn_lds + (async_x ? xb_bytes + scr_bytes : (xb_bytes > scr_bytes ? xb_bytes : scr_bytes)));
-    // direct global -> LDS loads: lane l of a wave fills chunk i0 + l
-    auto stage_x = [&]() {
-        for (int i0 = w * 64; i0 < nx; i0 += kGuWaves * 64) {
-            const int i = i0 + lane;
-            if (i < nx) {
-                const int c = i % cols, kg = i / cols;  // kg = ks * 4 + g
-                load_lds16(p.xB + ((size_t)kg * cstride + c) * 8, xs + i0);
-            }
-        }
+    // Direct global -> LDS copy of the operand (one contiguous block, as the
+    // column stride equals the column count) by waves w0 .. w0 + nws - 1;
+    // lane l of a wave fills chunk i0 + l.
+    auto stage_x = [&](int w0, int nws) {
+        if (w < w0) return;
+        for (int i0 = (w - w0) * 64; i0 < nx; i0 += nws * 64)
+            if (i0 + lane < nx) load_lds16(p.xB + (size_t)(i0 + lane) * 8, xs + i0);
     };
 
     int nslots;
     if (FUSED) {
-        if (async_x) stage_x();
+        // the waves without a token in the routing's first pass issue the copy
+        if (async_x) {
+            if (T < kGuWaves)
+                stage_x(T, kGuWaves - T);
+            else
+                stage_x(0, kGuWaves);
+        }
         // routing, recomputed by every workgroup (bit-identical results)
         block_route<kGuWaves * 64>(p, scr, sexp, tw_lds, &nslots_sh, blockIdx.x == 0);
         nslots = nslots_sh;
-        if (!async_x) stage_x();
+        if (!async_x) stage_x(0, kGuWaves);
     } else {
         nslots = min(p.meta[1], p.max_slots);
         for (int i = threadIdx.x; i < nslots; i += kGuWaves * 64)
             sexp[i] = min(max(p.slot_expert[i], 0), p.has_shared ? E : E - 1);
-        stage_x();
+        stage_x(0, kGuWaves);
     }
     wait_vm_all();
     __syncthreads();
@@ -417,92 +420,283 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// down: one workgroup of 8 waves per output row tile (16 rows of H).  The
-// workgroup streams the row tile of EVERY union slot (the waves take
-// interleaved batches of it), accumulating y for all tokens in registers
-// (the gate weights are already folded into the hidden activations); the
-// partial sums meet in LDS in a fixed order and the tile of y is written
-// once.  No atomics, no second pass, equal bytes per workgroup.
+// down: a unit is RG row tiles (16 rows of H each) x one k-unit of one union
+// slot.  A wave loads the unit's activation fragment once and multiplies it
+// by the RG weight tiles, so the activation loads per weight byte drop by RG.
+// The units (row group, slot, k-unit), row-group major, are split evenly
+// over the grid (one workgroup of 8 waves per compute unit), so every compute
+// unit streams the same bytes whatever the number of row groups.  Inside a
+// row-group segment the waves take interleaved batches, accumulate y for all
+// tokens in registers (the gate weights are already folded into the hidden
+// activations) and meet in LDS in a fixed order.  A workgroup that owns a
+// whole row group writes it to y; the pieces of a row group shared by
+// several workgroups go to the workspace with device-scope stores, and the
+// workgroup that completes the group's piece count adds the pieces in
+// workgroup order (device-scope loads) and writes y.  The result does not
+// depend on timing, and no workgroup waits for another.
 // ---------------------------------------------------------------------------
 constexpr int kDnWaves = 8;
 
+template <int WT, int NT>
+struct DnCfg {
+    static constexpr int RG = NT <= 2 || (WT == 0 && NT == 3) ? 2 : 1;    // row tiles per unit
+    static constexpr int KT = WT == 1 ? 64 : 32;                          // k per packed tile
+    static constexpr int NA = WT == 1 ? 2 : 1;                            // tile loads per row tile
+    static constexpr int NS = WT == 1 ? 4 : 1;                            // k-steps per unit
+    static constexpr int KU = WT == 0 && NT == 1 ? 2 : 1;                 // units per batch
+};
+
+template <int WT, int NT>
+struct DnBatch {
+    using C = DnCfg<WT, NT>;
+    u32x4 a[C::KU][C::RG][C::NA];
+    u32x4 b[C::KU][C::NS][NT];
+    float sc[C::KU];
+    bool on[C::KU];
+};
+
+// Products of one batch into acc[row tile][token tile]; skipped units
+// multiply zeros (no branch, so the waits before the products only count
+// loads issued before this batch's own).
+template <int WT, int NT>
+__device__ __forceinline__ void dn_compute(const DnBatch<WT, NT> &bt, f32x4 (&acc)[DnCfg<WT, NT>::RG][NT], bool valid) {
+    using C = DnCfg<WT, NT>;
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < C::KU; ++u) {
+        const bool on = valid && bt.on[u];
+        if (WT == 0) {
+#pragma unroll
+            for (int r = 0; r < C::RG; ++r) {
+                const bf16x8 a = as_bf16x8(on ? bt.a[u][r][0] : zero);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[r][n] = mfma(a, as_bf16x8(bt.b[u][0][n]), acc[r][n]);
+            }
+        } else {
+            const float sc = on ? bt.sc[u] : 0.f;
+#pragma unroll
+            for (int r = 0; r < C::RG; ++r) {
+                f32x4 t[2][NT];
+#pragma unroll
+                for (int n = 0; n < NT; ++n) t[0][n] = t[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    bf16x8 lo, hi;
+                    fp8x16_to_bf16(bt.a[u][r][h], lo, hi);
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) {
+                        t[0][n] = mfma(lo, as_bf16x8(bt.b[u][2 * h][n]), t[0][n]);
+                        t[1][n] = mfma(hi, as_bf16x8(bt.b[u][2 * h + 1][n]), t[1][n]);
+                    }
+                }
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[r][n] += sc * (t[0][n] + t[1][n]);
+            }
+        }
+    }
+}
+
+// Workgroup that owns unit u when W units are split over G workgroups as
+// [b W / G, (b + 1) W / G).
+__device__ __forceinline__ int unit_owner(long long u, long long W, int G) {
+    return (int)(((u + 1) * G - 1) / W);
+}
+
 template <int WT, int NT, bool SPLIT>
 __global__ __launch_bounds__(kDnWaves * 64) void down_kernel(VerifyParams p) {
-    using C = UnitCfg<WT, NT>;
-    constexpr int KU = C::KU;
-    using B = Batch<WT, NT, KU>;
-    __shared__ f32x4 red[kDnWaves][NT][64];
+    using C = DnCfg<WT, NT>;
+    using B = DnBatch<WT, NT>;
+    constexpr int RG = C::RG, KU = C::KU;
+    __shared__ f32x4 red[kDnWaves][RG][NT][64];
     __shared__ int sexp[kMaxExperts + 1];
+    __shared__ int last_sh;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = lane >> 4, lr = lane & 15;
     const int T = p.T, H = p.H, I = p.I, E = p.E, cstride = p.cstride;
     const int nkt = I / C::KT;
     const int rtiles = H / 16;
+    const int ngroups = (rtiles + RG - 1) / RG;
     const int nslots = min(p.meta[1], p.max_slots);
     const size_t esz = WT == 1 ? 1 : 2;
     const size_t bstep = (size_t)4 * cstride * 8;
     for (int i = threadIdx.x; i < nslots; i += kDnWaves * 64)
         sexp[i] = min(max(p.slot_expert[i], 0), p.has_shared ? E : E - 1);
     __syncthreads();
-    // Units (slot, k-unit) in slot-major order for one row tile; batches of KU
+    // Units of one row group: (slot, k-unit) slot-major; batches of KU
     // consecutive units go to the waves round-robin, so the workgroup reads
-    // one contiguous window that moves through the slots' row-tile segments.
+    // a window that moves through the slots' row-group segments.
     const int nunits = WT == 1 ? nkt / 2 : nkt;
-    const int total = nslots * nunits;
-    const int nbt = (total + KU - 1) / KU;
-    const int nbw = nbt > w ? (nbt - w + kDnWaves - 1) / kDnWaves : 0;  // this wave's batches
+    const long long per_group = (long long)nslots * nunits;
+    const long long W = per_group * ngroups;
+    const int G = gridDim.x, bid = blockIdx.x;
+    const long long u0 = (long long)bid * W / G, u1 = (long long)(bid + 1) * W / G;
     const int sld = I / 128;
     const uint16_t *hb0 = p.hB + (size_t)g * cstride * 8;
     int coff[NT];
     col_offsets<NT>(coff, lr, p.cols);
-    for (int rt = blockIdx.x; rt < rtiles; rt += gridDim.x) {
-        const size_t toff = (size_t)rt * nkt * 1024 + lane * 16;
-        const int srow = (16 * rt) / 128;
+    const int pstride = RG * T * 16;  // floats per piece slot
+    float *ypart = p.ypart + (size_t)bid * 2 * pstride;
+
+    for (long long a = u0; a < u1;) {
+        const int rg = (int)(a / per_group);
+        const long long tb = (long long)rg * per_group, te = tb + per_group;
+        const long long ae = u1 < te ? u1 : te;
+        const int qa = (int)(a - tb), qb = (int)(ae - tb);  // units [qa, qb) of row group rg
+        const int nbt = (qb - qa + KU - 1) / KU;
+        const int nbw = nbt > w ? (nbt - w + kDnWaves - 1) / kDnWaves : 0;  // this wave's batches
+        // row tiles of the group in the packed layout (groups of 4 row tiles,
+        // then K-tile, then the tile inside the group; a ragged last group
+        // re-reads its last tile for the missing ones and drops their outputs)
+        size_t toff[RG];
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const int rt = min(rg * RG + r, rtiles - 1);
+            toff[r] = ((size_t)(rt >> 2) * nkt * 4 + (rt & 3)) * 1024 + lane * 16;
+        }
+        const int srow = (16 * rg * RG) / 128;  // 128-row scale block of the group (16 RG <= 128)
+        // weight and scale bases of the slot being loaded, refreshed when the
+        // wave's units move to the next slot (units are slot-major)
+        int c_s = -1;
+        const uint8_t *c_wb = nullptr;
+        const float *c_sb = nullptr;
         auto load_batch = [&](B &bt, int f) {
-            const int q0 = (f * kDnWaves + w) * KU;
+            const int q0 = qa + (f * kDnWaves + w) * KU;
 #pragma unroll
             for (int u = 0; u < KU; ++u) {
                 const int q = q0 + u;
-                const bool on = q < total;
-                const int qc = on ? q : total - 1;
+                const bool on = q < qb;
+                const int qc = on ? q : qb - 1;
                 const int s = qc / nunits, kk = qc - s * nunits;
-                const int e = sexp[s];
-                const bool sh = e == E;
-                const uint8_t *wb = sh ? static_cast<const uint8_t *>(p.Wsh_d)
-                                       : static_cast<const uint8_t *>(p.W_d) + (size_t)e * H * I * esz;
-                const float scale = WT == 1 ? (sh ? p.ssh_d : p.s_d + (size_t)e * (H / 128) * sld)[srow * sld + kk] : 0.f;
-                load_unit<WT, NT, KU>(bt, u, on, wb + toff + (size_t)kk * C::USTEP,
-                                      hb0 + (size_t)s * I * cstride + (size_t)kk * C::KSTEPS * bstep, bstep, scale, coff);
+                if (s != c_s) {
+                    c_s = s;
+                    const int e = sexp[s];
+                    const bool sh = e == E;
+                    c_wb = sh ? static_cast<const uint8_t *>(p.Wsh_d)
+                              : static_cast<const uint8_t *>(p.W_d) + (size_t)e * H * I * esz;
+                    if (WT == 1) c_sb = (sh ? p.ssh_d : p.s_d + (size_t)e * (H / 128) * sld) + srow * sld;
+                }
+                // K-tile kk * NA + h of row tile r sits 4 KB per K-tile apart
+                const uint8_t *wb = c_wb + (size_t)kk * C::NA * 4096;
+                bt.on[u] = on;
+#pragma unroll
+                for (int r = 0; r < RG; ++r)
+#pragma unroll
+                    for (int h = 0; h < C::NA; ++h) bt.a[u][r][h] = ld_nt(wb + toff[r] + h * 4096);
+                const uint16_t *bq = hb0 + (size_t)s * I * cstride + (size_t)kk * C::NS * bstep;
+#pragma unroll
+                for (int q2 = 0; q2 < C::NS; ++q2)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+                        bt.b[u][q2][n] = *reinterpret_cast<const u32x4 *>(bq + q2 * bstep + coff[n]);
+                bt.sc[u] = WT == 1 ? c_sb[kk] : 0.f;
             }
         };
-        f32x4 acc2[2][NT];
+        f32x4 acc[RG][NT];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc2[0][n] = acc2[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 (&acc)[NT] = acc2[0];
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[r][n] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (nbw > 0) {
             B b0, b1;
             load_batch(b0, 0);
             for (int f = 0; f < nbw; f += 2) {
                 load_batch(b1, min(f + 1, nbw - 1));
-                compute_batch<WT, NT, KU>(b0, acc2, true);
+                dn_compute<WT, NT>(b0, acc, true);
                 load_batch(b0, min(f + 2, nbw - 1));
-                compute_batch<WT, NT, KU>(b1, acc2, f + 1 < nbw);
+                dn_compute<WT, NT>(b1, acc, f + 1 < nbw);
             }
         }
-        fold_acc<NT>(acc2);
-        reduce_waves<NT, kDnWaves>(acc, red, w, lane);
-        if (w == 0) {
-            float v[NT][4];
-            combine_split<NT, SPLIT>(v, acc, T, lane);
+        // partial sums of the waves meet in LDS in wave order
+        if (w != 0) {
 #pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const int t = n * 16 + lr;
-                if (t < T)
-                    *reinterpret_cast<float4 *>(p.y + (size_t)t * H + 16 * rt + 4 * g) =
-                        make_float4(v[n][0], v[n][1], v[n][2], v[n][3]);
+            for (int r = 0; r < RG; ++r)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) red[w][r][n][lane] = acc[r][n];
+        }
+        __syncthreads();
+        const bool whole = qa == 0 && qb == per_group;
+        const int first = whole ? 0 : unit_owner(tb, W, G), last = whole ? 0 : unit_owner(te - 1, W, G);
+        if (w == 0) {
+#pragma unroll
+            for (int q2 = 1; q2 < kDnWaves; ++q2)
+#pragma unroll
+                for (int r = 0; r < RG; ++r)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) acc[r][n] += red[q2][r][n][lane];
+            // a piece goes to this workgroup's slot (0 for its first row
+            // group, 1 for its last)
+            float *dst = ypart + (a == u0 ? 0 : pstride) + 4 * g;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                float v[NT][4];
+                combine_split<NT, SPLIT>(v, acc[r], T, lane);
+                const int rt = rg * RG + r;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const int t = n * 16 + lr;
+                    if (t >= T) continue;
+                    if (whole) {
+                        if (rt < rtiles)
+                            *reinterpret_cast<float4 *>(p.y + (size_t)t * H + 16 * rt + 4 * g) =
+                                make_float4(v[n][0], v[n][1], v[n][2], v[n][3]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            __hip_atomic_store(dst + (size_t)(r * T + t) * 16 + j, v[n][j], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+            if (!whole) {
+                // once the piece's stores have completed, the group's piece
+                // counter counts it
+                wait_vm_all();
+                if (lane == 0) {
+                    // pieces = workgroups in [first, last] with a non-empty range
+                    int np = 0;
+                    for (int ob = first; ob <= last; ++ob)
+                        np += (long long)ob * W / G < (long long)(ob + 1) * W / G ? 1 : 0;
+                    last_sh = __hip_atomic_fetch_add(p.tile_cnt + rg, 1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT) == np - 1;
+                }
+            }
+        }
+        if (!whole) {
+            __syncthreads();
+            if (last_sh && w == 0) {
+                // every piece is complete: add them in workgroup order; a
+                // workgroup's slot is 0 when this row group is its first one
+#pragma unroll
+                for (int r = 0; r < RG; ++r) {
+                    const int rt = rg * RG + r;
+                    float v[NT][4] = {};
+                    for (int ob = first; ob <= last; ++ob) {
+                        const long long os = (long long)ob * W / G;
+                        if (os == (long long)(ob + 1) * W / G) continue;  // empty range: no piece
+                        const float *src = p.ypart + (size_t)ob * 2 * pstride + (os / per_group == rg ? 0 : pstride) +
+                                           (size_t)r * T * 16 + 4 * g;
+#pragma unroll
+                        for (int n = 0; n < NT; ++n) {
+                            const int t = n * 16 + lr;
+                            if (t < T)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    v[n][j] += __hip_atomic_load(src + (size_t)t * 16 + j, __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                    }
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) {
+                        const int t = n * 16 + lr;
+                        if (t < T && rt < rtiles)
+                            *reinterpret_cast<float4 *>(p.y + (size_t)t * H + 16 * rt + 4 * g) =
+                                make_float4(v[n][0], v[n][1], v[n][2], v[n][3]);
+                    }
+                }
             }
         }
         __syncthreads();
+        a = ae;
     }
 }
 
@@ -596,13 +790,6 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyParams p) {
     }
 }
 
-// Persistent grid: `per_cu` workgroups per compute unit, at most what fits.
-template <typename K>
-int resident_grid(K kernel, int threads, int n_cu, int per_cu, size_t dyn_lds) {
-    int fit = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&fit, kernel, threads, dyn_lds) != hipSuccess || fit < 1) fit = 1;
-    return (per_cu < fit ? per_cu : fit) * n_cu;
-}
 
 // LDS plan of the gate-up kernel: routing fused into its prologue and the
 // activation operand held in LDS when they fit in one compute unit.
@@ -644,10 +831,9 @@ hipError_t launch_one(const VerifyParams &p, int n_cu, hipStream_t s, KernelEven
         if (pl.fused) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, false>, q, pl.dyn, n_cu, s, ev);
         return launch_gu(gateup_kernel<WT, NT, SPLIT, false, false>, q, 0, n_cu, s, ev);
     } else {
-        auto kernel = down_kernel<WT, NT, SPLIT>;
-        static const int cap = resident_grid(kernel, kDnWaves * 64, n_cu, kDownWgPerCu, 0);
-        const int rtiles = p.H / 16;  // one workgroup per row tile when they all fit at once
-        return launch_k(kernel, dim3(rtiles < cap ? rtiles : cap), dim3(kDnWaves * 64), 0, s, ev, p);
+        // one workgroup per compute unit; the work splits evenly over them
+        const int grid = n_cu < kDownMaxGrid ? n_cu : kDownMaxGrid;
+        return launch_k(down_kernel<WT, NT, SPLIT>, dim3(grid), dim3(kDnWaves * 64), 0, s, ev, p);
     }
 }
 

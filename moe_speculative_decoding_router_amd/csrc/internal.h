@@ -43,7 +43,9 @@ struct VerifyParams {
     uint16_t *xB;      // [H * cols] bf16 activations in the matrix-core operand order
     uint16_t *hB;      // [max_slots * I * cols] bf16 hidden activations, weighted
     float *h32;        // [max_slots * T * I] float32 hidden (float32 weights)
-    float *ydown;      // [(T * k + T) * H] per-(token, expert) outputs
+    float *ydown;      // [(T * k + T) * H] per-(token, expert) outputs (float32 weights)
+    float *ypart;      // [kDownMaxGrid * 2 * kDownMaxRowTiles * T * 16] down: partial row groups (bf16 / fp8)
+    int *tile_cnt;     // [H / 16] down: pieces finished per row group (zeroed by the router kernel)
 };
 
 constexpr int kWaveSize = 64;
@@ -82,6 +84,8 @@ hipError_t launch_select(int N, const float *P, const uint32_t *F, int W, int ga
 constexpr int kMaxTokens = 64;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
+constexpr int kDownMaxGrid = 1024;    // workgroups of the matrix-core down kernel
+constexpr int kDownMaxRowTiles = 4;  // row tiles per down work unit
 constexpr int kSelectMaxLdsWords = 16384;  // 64 KB of footprint words per tree
 
 }  // namespace moe

@@ -42,7 +42,7 @@ int cu_count() {
 
 struct Layout {
     size_t logits, topk_idx, topk_w, meta, union_experts, csr_ptr, csr_tok, csr_w, pstar;
-    size_t slot_expert, tokw, tokpos, tpos, xB, hB, h32, ydown, total;
+    size_t slot_expert, tokw, tokpos, tpos, xB, hB, h32, ydown, ypart, tile_cnt, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -77,14 +77,16 @@ Layout make_layout(const moe_layer &L, int T) {
     o.tokpos = take(slots * T * 4);
     o.tpos = take(T * k * 4);
     if (L.wdtype == MOE_F32) {
-        o.xB = o.hB = 0;
+        o.xB = o.hB = o.ypart = o.tile_cnt = 0;
         o.h32 = take(slots * T * I * 4);
+        o.ydown = take(((size_t)T * k + T) * H * 4);
     } else {
         o.xB = take(H * cstride * 2);
         o.hB = take(slots * I * cstride * 2);
-        o.h32 = 0;
+        o.h32 = o.ydown = 0;
+        o.ypart = take((size_t)moe::kDownMaxGrid * 2 * moe::kDownMaxRowTiles * T * 16 * 4);
+        o.tile_cnt = take((H / 16 + 1) * 4);
     }
-    o.ydown = take(((size_t)T * k + T) * H * 4);
     o.total = off;
     return o;
 }
@@ -98,8 +100,8 @@ int validate_layer(const moe_layer *L, int T, const moe_bias *bias) {
         return fail(MOE_EINVAL, "k=%d outside [1, min(E, %d)]", L->k, MOE_MAX_TOPK);
     if (L->wdtype != MOE_F32 && L->wdtype != MOE_BF16 && L->wdtype != MOE_FP8_E4M3)
         return fail(MOE_EINVAL, "unknown wdtype %d", L->wdtype);
-    if (L->wdtype == MOE_BF16 && (L->H % 32 != 0 || L->I % 32 != 0))
-        return fail(MOE_ENOTSUP, "bf16 weights need H and I multiples of 32 (H=%d, I=%d)", L->H, L->I);
+    if (L->wdtype == MOE_BF16 && (L->H % 64 != 0 || L->I % 32 != 0))
+        return fail(MOE_ENOTSUP, "bf16 weights need H a multiple of 64 and I of 32 (H=%d, I=%d)", L->H, L->I);
     if (L->wdtype == MOE_FP8_E4M3 && (L->H % 128 != 0 || L->I % 128 != 0))
         return fail(MOE_ENOTSUP, "fp8 weights need H and I multiples of 128 (H=%d, I=%d)", L->H, L->I);
     if ((size_t)L->E * 2 * L->I * (size_t)L->H > ((size_t)1 << 40))
@@ -200,7 +202,9 @@ int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const mo
     p.xB = L.wdtype == MOE_F32 ? nullptr : reinterpret_cast<uint16_t *>(w + lay.xB);
     p.hB = L.wdtype == MOE_F32 ? nullptr : reinterpret_cast<uint16_t *>(w + lay.hB);
     p.h32 = L.wdtype == MOE_F32 ? reinterpret_cast<float *>(w + lay.h32) : nullptr;
-    p.ydown = reinterpret_cast<float *>(w + lay.ydown);
+    p.ydown = L.wdtype == MOE_F32 ? reinterpret_cast<float *>(w + lay.ydown) : nullptr;
+    p.ypart = L.wdtype == MOE_F32 ? nullptr : reinterpret_cast<float *>(w + lay.ypart);
+    p.tile_cnt = L.wdtype == MOE_F32 ? nullptr : reinterpret_cast<int *>(w + lay.tile_cnt);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int ncu = cu_count();
@@ -242,6 +246,7 @@ int moe_pack_weights(const void *src, void *dst, int32_t E, int32_t rows, int32_
     if (rows % 16 != 0 || K % kt != 0)
         return fail(MOE_EINVAL, "rows must be a multiple of 16 and K of %d", kt);
     if (gate_up && rows % 32 != 0) return fail(MOE_EINVAL, "gate-up rows (2I) must be a multiple of 32");
+    if (!gate_up && rows % 64 != 0) return fail(MOE_EINVAL, "down rows (H) must be a multiple of 64");
     const size_t esz = wdtype == MOE_BF16 ? 2 : 1;
     const size_t bytes = (size_t)E * rows * K * esz;
     const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);

@@ -6,10 +6,14 @@
 // [8 g, 8 g + 8) (bf16) or [16 g, 16 g + 16) (fp8) of the tile, g = l / 16:
 // exactly the A operand of v_mfma_f32_16x16x32_bf16 for lane l, so one
 // 16-byte load per lane reads 1 KB of contiguous memory per wave.  Tiles are
-// ordered row-tile major, K-tile minor, so one row tile is one contiguous
-// stream.  For gate/up matrices a row tile interleaves 8 gate rows (tile rows
-// 0..7) with the 8 up rows of the same intermediate indices (tile rows 8..15),
-// so one tile yields both halves of SwiGLU for 8 intermediate indices.
+// ordered row-tile major, K-tile minor for the gate/up matrices, so one row
+// tile is one contiguous stream; there a row tile interleaves 8 gate rows
+// (tile rows 0..7) with the 8 up rows of the same intermediate indices (tile
+// rows 8..15), so one tile yields both halves of SwiGLU for 8 intermediate
+// indices.  The down matrices are ordered in groups of 4 row tiles (64
+// rows): group major, then K-tile, then the row tile inside the group, so the
+// 4 row tiles that share an activation fragment are one contiguous 4 KB
+// (bf16) block per K-tile.
 #include "common.h"
 #include "internal.h"
 
@@ -28,13 +32,21 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ s
         const long long rem = q - e * per_expert;
         const int l = (int)(rem & 63);
         const long long tile = rem >> 6;
-        const int rt = (int)(tile / nkt), kt = (int)(tile - (long long)rt * nkt);
         const int m = l & 15, g = l >> 4;
-        int row;
-        if (interleave)
+        int row, kt;
+        if (interleave) {
+            // gate-up: row tile major, then K-tile; 8 gate rows + 8 up rows
+            const int rt = (int)(tile / nkt);
+            kt = (int)(tile - (long long)rt * nkt);
             row = m < 8 ? 8 * rt + m : half + 8 * rt + (m - 8);
-        else
-            row = 16 * rt + m;
+        } else {
+            // down: groups of 4 row tiles (64 rows), then K-tile, then the
+            // row tile inside the group
+            const int grp = (int)(tile / (4LL * nkt));
+            const int rem2 = (int)(tile - (long long)grp * 4 * nkt);
+            kt = rem2 >> 2;
+            row = 16 * (4 * grp + (rem2 & 3)) + m;
+        }
         const int k = kt * KT + g * (KT / 4);
         const u32x4 v = *reinterpret_cast<const u32x4 *>(src + ((e * R + row) * (long long)K + k) * esz);
         *reinterpret_cast<u32x4 *>(dst + q * 16) = v;

@@ -52,7 +52,7 @@ def test_workspace_bytes_and_shape_validation(lib):
     assert ws_bytes(lib, layer(), 5) > 0
     assert ws_bytes(lib, layer(), 64) > ws_bytes(lib, layer(), 5)
     for bad in (dict(k=0), dict(k=33, E=64), dict(k=40, E=32), dict(E=513), dict(H=0), dict(wdtype=7),
-                dict(H=500), dict(I=250), dict(wdtype=m.MOE_FP8_E4M3, H=512, I=192)):
+                dict(H=500), dict(H=544), dict(I=250), dict(wdtype=m.MOE_FP8_E4M3, H=512, I=192)):
         assert ws_bytes(lib, layer(**bad), 5) == 0, bad
     assert ws_bytes(lib, layer(), 0) == 0 and ws_bytes(lib, layer(), 65) == 0
     b = m._Bias(3, 0.5, 16)                       # cap < k

@@ -95,24 +95,27 @@ def expected_pack(src, gate_up, esz):
     b = src.view(np.uint8).reshape(E, R, K * esz)
     q = 0
     for e in range(E):
-        for rt in range(R // 16):
-            for kt in range(K // KT):
-                for l in range(64):
-                    m_, g = l % 16, l // 16
-                    if gate_up:
-                        row = 8 * rt + m_ if m_ < 8 else R // 2 + 8 * rt + (m_ - 8)
-                    else:
-                        row = 16 * rt + m_
-                    k = kt * KT + g * (KT // 4)
-                    out[q * 16:(q + 1) * 16] = b[e, row, k * esz:k * esz + 16]
-                    q += 1
+        if gate_up:   # row tile major, then K-tile
+            order = [(rt, kt) for rt in range(R // 16) for kt in range(K // KT)]
+        else:         # groups of 4 row tiles, then K-tile, then the tile in the group
+            order = [(4 * grp + r, kt) for grp in range(R // 64) for kt in range(K // KT) for r in range(4)]
+        for rt, kt in order:
+            for l in range(64):
+                m_, g = l % 16, l // 16
+                if gate_up:
+                    row = 8 * rt + m_ if m_ < 8 else R // 2 + 8 * rt + (m_ - 8)
+                else:
+                    row = 16 * rt + m_
+                k = kt * KT + g * (KT // 4)
+                out[q * 16:(q + 1) * 16] = b[e, row, k * esz:k * esz + 16]
+                q += 1
     return out
 
 
 @pytest.mark.parametrize("wdtype,gate_up", [("bf16", True), ("bf16", False), ("fp8", True), ("fp8", False)])
 def test_pack_layout(wdtype, gate_up):
     rng = np.random.default_rng(7)
-    E, R, K = 2, 64, 256
+    E, R, K = 2, 128, 256
     if wdtype == "bf16":
         src = rng.integers(0, 1 << 16, size=(E, R, K), dtype=np.uint16)
         t = to_dev(src.view(np.int16))
