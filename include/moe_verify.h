@@ -159,7 +159,7 @@ size_t moe_verify_workspace_bytes(const moe_layer *layer, int32_t T, const moe_b
  * Limits: 1 <= T <= 64, 1 <= k <= min(E, 32), E <= 512; bf16: H a multiple of
  * 64 and I of 32; fp8: H, I multiples of 128.  Numerics: router GEMV and FFN
  * accumulate in float32; activations enter the bf16/fp8 matrix-core
- * products as a bf16 high/low pair when T <= 32 (as one bf16 otherwise). */
+ * products as a bf16 high/low pair when T <= 8 (as one bf16 otherwise). */
 int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const moe_bias *bias,
                      float *y, moe_aux *aux, void *ws, size_t ws_bytes, void *stream);
 

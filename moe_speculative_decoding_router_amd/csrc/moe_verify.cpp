@@ -47,9 +47,11 @@ struct Layout {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Activations enter the matrix-core products as a bf16 high/low pair while
-// the 2T columns fit in four 16-column tiles.
-bool split_mode(int T) { return 2 * T <= 64; }
+// Activations enter the matrix-core products as a bf16 high/low pair (about
+// float32 accuracy) while the 2T columns fit in one 16-column tile; beyond
+// that they enter as plain bf16, which keeps the operand traffic per weight
+// tile at one tile per 16 tokens.
+bool split_mode(int T) { return 2 * T <= 16; }
 
 Layout make_layout(const moe_layer &L, int T) {
     Layout o{};
