@@ -15,6 +15,7 @@ docstrings:
               expert union, token-by-expert CSR, per-token dense MoE layer,
               per-layer union statistics;
 * ``select``  EcoSpec cost-aware greedy draft selection;
+* ``expand``  S^2-MoE utility-driven adaptive expansion of a draft tree;
 * ``fp``      bf16 and OCP FP8 E4M3FN decoding from their definitions.
 
 Parity status: every function is pinned by CPU tests against closed forms,
@@ -23,4 +24,4 @@ of the reuse-bias steps (importance g, TopCap, bias size), whose formulas are
 missing from the page; that part is pinned to the stated reading and to the
 page's qualitative example only ("parity pinned to the reading").
 """
-from . import fp, moe, select  # noqa: F401
+from . import expand, fp, moe, select  # noqa: F401
