@@ -189,6 +189,31 @@ int union_stats(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32
 int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred,
                   int32_t W, int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream);
 
+/* Utility-driven adaptive expansion of draft trees ([S2-MoE] component 1,
+ * routing-aware adaptive speculative expansion).  Per tree, a draft token i
+ * joins the expansion set S while its utility
+ *     U_i = p_i * T_AR / (|E_i \ union_{j in S} E_j| * T_exp + C_i^draft)
+ * is at least 1: candidates are examined in generation (BFS) order, a node
+ * only once its parent is in S (or it is a child of the root), and passes
+ * repeat until one adds no node.  The test is evaluated in float32 as
+ * fl(p * t_ar) >= fl(fl(c * t_exp) + c_draft) with the exact count c of new
+ * (layer, expert) pairs; the resulting set does not depend on the order.
+ *   parent  (host) [N] int32, BFS order, -1 = child of the root, parent < child
+ *   P       [nt, N] float32 acceptance probabilities (e.g. path probabilities)
+ *   Epred   [nt, N, W] uint32 footprint bitsets, as for select_drafts (own or
+ *           whole-path footprints give the same result, since S is
+ *           prefix-closed)
+ *   t_ar    saving of one accepted token (one autoregressive step), >= 0
+ *   t_exp   latency of one new (layer, expert) pair, >= 0
+ *   c_draft [nt, N] float32 draft-side cost of each node, or NULL (zero)
+ *   S       [nt, N] int32 out: nodes in the order they join, then -1
+ *   count   [nt] int32 out: size of each set
+ * Limits: N <= 1024 and N * W + W + 3 N + N / 32 <= 16384 words (LDS stage).
+ * Errors: EINVAL (NULL, shapes, parent order, t_ar / t_exp), ENOTSUP (LDS). */
+int expand_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred, int32_t W,
+                  float t_ar, float t_exp, const float *c_draft, int32_t nt, int32_t *S, int32_t *count,
+                  void *stream);
+
 /* Message for the calling thread's last non-zero return ("" if none). */
 const char *moe_last_error(void);
 

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI in include/moe_verify.h):
   verify_layer(x, layer, bias=None)   -> (y, aux)
   union_stats(topk_idx, E)            -> (counts, reuse)
   select_drafts(parent, P, Epred, gamma, eps=1e-6) -> S
+  expand_drafts(parent, P, Epred, t_ar, t_exp, c_draft=None) -> (S, count)
   workspace_bytes(layer, T, bias=None)
 """
 from __future__ import annotations
@@ -29,7 +30,7 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 NUM_STAGES = 5
 STAGE_NAMES = ("router", "route", "gate_up", "down", "combine")
 EXPORTED = ("moe_pack_weights", "moe_verify_workspace_bytes", "moe_verify_layer", "union_stats",
-            "select_drafts", "moe_last_error")
+            "select_drafts", "expand_drafts", "moe_last_error")
 
 _vp, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.union_stats.restype = ctypes.c_int
         L.select_drafts.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _vp]
         L.select_drafts.restype = ctypes.c_int
+        L.expand_drafts.argtypes = [_vp, _i32, _vp, _vp, _i32, _f32, _f32, _vp, _i32, _vp, _vp, _vp]
+        L.expand_drafts.restype = ctypes.c_int
         L.moe_pack_weights.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
         L.moe_pack_weights.restype = ctypes.c_int
         L.moe_last_error.argtypes = []
@@ -290,3 +293,30 @@ def select_drafts(parent, P, Epred, gamma: int, eps: float = 1e-6, out=None, str
     _check(lib().select_drafts(par.ctypes.data, N, P.data_ptr(), Epred.data_ptr(), W, gamma, eps, nt,
                                S.data_ptr(), s))
     return S
+
+
+def expand_drafts(parent, P, Epred, t_ar: float, t_exp: float, c_draft=None, stream=None):
+    """S2-MoE utility-driven expansion for nt trees: parent (host) [N], P [nt, N]
+    float32, Epred [nt, N, W] 32-bit and c_draft [nt, N] float32 or None
+    (device).  Returns (S [nt, N] int32 join order padded with -1, count [nt]
+    int32), both on the device."""
+    import torch
+    par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+    if P.dtype != torch.float32 or P.dim() != 2 or not P.is_contiguous():
+        raise ValueError("P must be a contiguous float32 [nt, N] tensor")
+    if Epred.dim() != 3 or Epred.element_size() != 4 or not Epred.is_contiguous():
+        raise ValueError("Epred must be a contiguous 32-bit [nt, N, W] tensor")
+    nt, N = (int(v) for v in P.shape)
+    if tuple(Epred.shape[:2]) != (nt, N) or par.shape != (N,):
+        raise ValueError("shape mismatch between parent, P and Epred")
+    if c_draft is not None and (c_draft.dtype != torch.float32 or tuple(c_draft.shape) != (nt, N)
+                                or not c_draft.is_contiguous()):
+        raise ValueError("c_draft must be a contiguous float32 [nt, N] tensor")
+    W = int(Epred.shape[2])
+    S = torch.empty((nt, N), dtype=torch.int32, device=P.device)
+    count = torch.empty((nt,), dtype=torch.int32, device=P.device)
+    s = stream if stream is not None else torch.cuda.current_stream(P.device).cuda_stream
+    _check(lib().expand_drafts(par.ctypes.data, N, P.data_ptr(), Epred.data_ptr(), W, t_ar, t_exp,
+                               c_draft.data_ptr() if c_draft is not None else None, nt, S.data_ptr(),
+                               count.data_ptr(), s))
+    return S, count

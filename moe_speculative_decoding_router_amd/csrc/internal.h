@@ -80,6 +80,17 @@ hipError_t launch_union_stats(const int32_t *topk_idx, int nL, int T, int k, int
 hipError_t launch_select(int N, const float *P, const uint32_t *F, int W, int gamma, float eps,
                          int nt, int32_t *S, hipStream_t s);
 
+// Arguments of the expansion kernel (parents by value: no device copy).
+constexpr int kMaxExpandNodes = 1024;
+struct ExpandArgs {
+    int N, W, nt, tpn;
+    float t_ar, t_exp;
+    int16_t parent[kMaxExpandNodes];
+};
+size_t expand_lds_bytes(int N, int W);
+hipError_t launch_expand(ExpandArgs a, const float *P, const uint32_t *F, const float *Cd, int32_t *S,
+                         int32_t *count, hipStream_t s);
+
 // Limits used by the kernels.
 constexpr int kMaxTokens = 64;
 constexpr int kMaxExperts = 512;

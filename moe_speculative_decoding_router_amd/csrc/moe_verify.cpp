@@ -293,4 +293,34 @@ int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32
     return MOE_OK;
 }
 
+
+int expand_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred, int32_t W, float t_ar,
+                  float t_exp, const float *c_draft, int32_t nt, int32_t *S, int32_t *count, void *stream) {
+    if (!parent) return fail(MOE_EINVAL, "parent is NULL");
+    if (N < 1 || N > moe::kMaxExpandNodes) return fail(MOE_EINVAL, "N=%d outside [1, %d]", N, moe::kMaxExpandNodes);
+    if (W < 1 || W > 4096) return fail(MOE_EINVAL, "W=%d outside [1, 4096]", W);
+    if (!std::isfinite(t_ar) || !std::isfinite(t_exp) || t_ar < 0.f || t_exp < 0.f)
+        return fail(MOE_EINVAL, "t_ar and t_exp must be finite and non-negative");
+    if (nt < 0) return fail(MOE_EINVAL, "nt=%d is negative", nt);
+    moe::ExpandArgs a{};
+    for (int i = 0; i < N; ++i) {
+        if (parent[i] < -1 || parent[i] >= i)
+            return fail(MOE_EINVAL, "parent[%d]=%d: nodes must be in BFS order (parent < child)", i, parent[i]);
+        a.parent[i] = (int16_t)parent[i];
+    }
+    if (moe::expand_lds_bytes(N, W) > (size_t)moe::kSelectMaxLdsWords * 4)
+        return fail(MOE_ENOTSUP, "tree footprint of %d x %d words exceeds the %d-word LDS stage", N, W,
+                    moe::kSelectMaxLdsWords);
+    if (nt == 0) return MOE_OK;
+    if (!P || !Epred || !S || !count) return fail(MOE_EINVAL, "NULL pointer");
+    a.N = N;
+    a.W = W;
+    a.nt = nt;
+    a.t_ar = t_ar;
+    a.t_exp = t_exp;
+    hipError_t err = moe::launch_expand(a, P, Epred, c_draft, S, count, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(MOE_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return MOE_OK;
+}
+
 }  // extern "C"

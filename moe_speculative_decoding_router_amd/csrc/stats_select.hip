@@ -5,6 +5,8 @@
 // [EcoSpec] = review of "Less Experts, Faster Decoding": §3.2 (global expert
 // buffer B, rebuilt from empty every step) and §3.3 (score = path
 // probability / (new (layer, expert) pairs + eps), greedy gamma times).
+// [S2-MoE] component 1 = routing-aware adaptive expansion: a draft token
+// joins while p * T_AR >= (new experts) * T_exp + draft cost.
 #include "common.h"
 #include "internal.h"
 
@@ -123,12 +125,119 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int N, const float 
     }
 }
 
+
+// One workgroup (256 threads) per tree.  Every round, groups of TPN threads
+// count the new pairs popcount(F & ~B) of all nodes outside S in parallel;
+// wave 0 then takes, in generation order from the scan position, the first
+// node whose parent is in S (or is the root) and whose utility test passes:
+//     fl(p * T_AR) >= fl(fl(c * T_exp) + C_draft)
+// (float32, no fused multiply-add).  The node joins S and its footprint is
+// added to B.  When no node from the scan position passes, a new pass starts
+// from node 0 if the last pass added a node, else the tree is done: at most
+// 2 N + 1 rounds, and every wave sees the same decision.
+__global__ __launch_bounds__(kSelThreads) void expand_kernel(ExpandArgs a, const float *__restrict__ P,
+                                                             const uint32_t *__restrict__ F,
+                                                             const float *__restrict__ Cd, int32_t *S,
+                                                             int32_t *count) {
+    extern __shared__ uint32_t lds[];
+    const int N = a.N, W = a.W;
+    uint32_t *Fs = lds;                                          // [N * W]
+    uint32_t *Bs = Fs + (size_t)N * W;                           // [W]
+    float *Ps = reinterpret_cast<float *>(Bs + W);               // [N]
+    float *Cs = Ps + N;                                          // [N]
+    int *cnt = reinterpret_cast<int *>(Cs + N);                  // [N]
+    uint32_t *inS = reinterpret_cast<uint32_t *>(cnt + N);       // [ceil(N / 32)]
+    __shared__ int pick_sh;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tree = blockIdx.x;
+    if (tree >= a.nt) return;
+    const uint32_t *Ft = F + (size_t)tree * N * W;
+    for (int i = tid; i < N * W; i += kSelThreads) Fs[i] = Ft[i];
+    for (int i = tid; i < W; i += kSelThreads) Bs[i] = 0u;
+    for (int i = tid; i < N; i += kSelThreads) {
+        Ps[i] = P[(size_t)tree * N + i];
+        Cs[i] = Cd ? Cd[(size_t)tree * N + i] : 0.f;
+    }
+    for (int i = tid; i < (N + 31) / 32; i += kSelThreads) inS[i] = 0u;
+    __syncthreads();
+
+    const int tpn = a.tpn;
+    const int grp = tid / tpn, sub = tid - grp * tpn, ngrp = kSelThreads / tpn;
+    int pos = 0, nsel = 0;
+    bool added = false;
+    for (int round = 0; round <= 2 * N; ++round) {
+        // ---- new pairs of every node outside S ----
+        for (int n0 = 0; n0 < N; n0 += ngrp) {
+            const int n = n0 + grp;
+            int c = 0;
+            if (n < N && !((inS[n >> 5] >> (n & 31)) & 1u))
+                for (int i = sub; i < W; i += tpn) c += __popc(Fs[(size_t)n * W + i] & ~Bs[i]);
+            for (int off = tpn >> 1; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+            if (n < N && sub == 0) cnt[n] = c;
+        }
+        __syncthreads();
+        // ---- wave 0: first passing node at or after the scan position ----
+        if (wv == 0) {
+            int pick = -1;
+            for (int base = pos; base < N && pick < 0; base += 64) {
+                const int n = base + lane;
+                bool ok = false;
+                if (n < N && !((inS[n >> 5] >> (n & 31)) & 1u)) {
+                    const int par = a.parent[n];
+                    if (par < 0 || ((inS[par >> 5] >> (par & 31)) & 1u)) {
+                        const float num = __fmul_rn(Ps[n], a.t_ar);
+                        const float den = __fadd_rn(__fmul_rn((float)cnt[n], a.t_exp), Cs[n]);
+                        ok = num >= den;
+                    }
+                }
+                const unsigned long long bal = __ballot(ok);
+                if (bal) pick = base + __ffsll((long long)bal) - 1;
+            }
+            if (lane == 0) {
+                if (pick >= 0) {
+                    inS[pick >> 5] |= 1u << (pick & 31);
+                    S[(size_t)tree * N + nsel] = pick;
+                } else if (added) {
+                    pick = -2;  // a new pass from node 0
+                }
+                pick_sh = pick;
+            }
+        }
+        __syncthreads();
+        const int pick = pick_sh;
+        if (pick == -1) break;
+        if (pick == -2) {
+            pos = 0;
+            added = false;
+        } else {
+            for (int i = tid; i < W; i += kSelThreads) Bs[i] |= Fs[(size_t)pick * W + i];
+            pos = pick + 1;
+            added = true;
+            ++nsel;
+        }
+        __syncthreads();
+    }
+    for (int i = nsel + tid; i < N; i += kSelThreads) S[(size_t)tree * N + i] = -1;
+    if (tid == 0) count[tree] = nsel;
+}
 }  // namespace
 
 hipError_t launch_union_stats(const int32_t *topk_idx, int nL, int T, int k, int E, int32_t *counts,
                               float *reuse, hipStream_t s) {
     const size_t lds = (size_t)((E + 31) / 32) * 4;
     hipLaunchKernelGGL(union_stats_kernel, dim3(nL), dim3(256), lds, s, topk_idx, T, k, E, counts, reuse);
+    return hipGetLastError();
+}
+
+size_t expand_lds_bytes(int N, int W) { return ((size_t)N * W + W + 3 * (size_t)N + (N + 31) / 32) * 4; }
+
+hipError_t launch_expand(ExpandArgs a, const float *P, const uint32_t *F, const float *Cd, int32_t *S,
+                         int32_t *count, hipStream_t s) {
+    int tpn = 1;
+    while (tpn * 2 <= 64 && tpn * 2 * a.N <= kSelThreads) tpn *= 2;
+    a.tpn = tpn;
+    hipLaunchKernelGGL(expand_kernel, dim3(a.nt), dim3(kSelThreads), expand_lds_bytes(a.N, a.W), s, a, P, F, Cd,
+                       S, count);
     return hipGetLastError();
 }
 

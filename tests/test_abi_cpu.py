@@ -98,6 +98,22 @@ def test_union_stats_and_select_validation(lib):
     assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4, 4, 1e-6, 0, 16, None) == 0    # no trees
 
 
+def test_expand_validation(lib):
+    par = np.array([-1, -1, 0, 0, 1, 1], dtype=np.int32)
+    bad = np.array([-1, 2, 0, 0, 1, 1], dtype=np.int32)
+    ok = lambda *a: lib.expand_drafts(*a)  # noqa: E731
+    assert ok(None, 6, 16, 16, 4, 1.0, 1.0, None, 1, 16, 16, None) == -1               # parent NULL
+    assert ok(bad.ctypes.data, 6, 16, 16, 4, 1.0, 1.0, None, 1, 16, 16, None) == -1    # BFS order
+    assert b"BFS" in lib.moe_last_error()
+    assert ok(par.ctypes.data, 6, 16, 16, 4, -1.0, 1.0, None, 1, 16, 16, None) == -1   # t_ar < 0
+    assert ok(par.ctypes.data, 6, 16, 16, 4, 1.0, float("inf"), None, 1, 16, 16, None) == -1
+    assert ok(par.ctypes.data, 6, 16, 16, 4000, 1.0, 1.0, None, 1, 16, 16, None) == -2  # LDS stage
+    assert ok(par.ctypes.data, 6, None, 16, 4, 1.0, 1.0, None, 1, 16, 16, None) == -1   # P NULL
+    assert ok(par.ctypes.data, 6, None, None, 4, 1.0, 1.0, None, 0, None, None, None) == 0  # no trees
+    big = np.full(1025, -1, dtype=np.int32)
+    assert ok(big.ctypes.data, 1025, 16, 16, 1, 1.0, 1.0, None, 1, 16, 16, None) == -1  # N > 1024
+
+
 def test_expert_bytes_matches_page_figures():
     import json
     with open(os.path.join(ROOT, "tests", "golden", "page_figures.json")) as f:

@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 import synth
+from oracle import expand as oexp
 from oracle import moe as omoe
 from oracle import select as osel
 
@@ -58,6 +59,31 @@ def test_select_large_batch_sampled():
             p = trees.parent[t]
             assert p < 0 or p in seen
             seen.add(int(t))
+
+
+@pytest.mark.parametrize("t_ar,t_exp,with_cd", [(300.0, 1.0, True), (600.0, 1.0, False), (40.0, 0.05, True),
+                                                (1.0, 0.0, False), (0.0, 1.0, True)])
+def test_expand_gptoss_trees(t_ar, t_exp, with_cd):
+    log(f"case expand_drafts gptoss trees nt=256 t_ar={t_ar} t_exp={t_exp} c_draft={with_cd}")
+    trees = synth.draft_trees(seed=4, nt=256, n_layers=36, E=128, k=4)
+    cd = (np.random.default_rng(9).uniform(0, 20, trees.P.shape).astype(np.float32) if with_cd
+          else np.zeros(trees.P.shape, np.float32))
+    S, cnt = m.expand_drafts(trees.parent, to_dev(trees.P), to_dev(trees.F.view(np.int32)), t_ar, t_exp,
+                             to_dev(cd) if with_cd else None)
+    torch.cuda.synchronize()
+    ref = oexp.expand_batch(trees.parent, trees.P, trees.F, t_ar, t_exp, cd)
+    assert np.array_equal(S.cpu().numpy(), ref)
+    assert np.array_equal(cnt.cpu().numpy(), (ref >= 0).sum(axis=1))
+    log(f"    nodes per tree: mean {float((ref >= 0).sum(axis=1).mean()):.2f}")
+
+
+def test_expand_odd_shapes():
+    log("case expand_drafts odd W, deep trees")
+    trees = synth.draft_trees(seed=6, nt=32, depth=5, branch=2, n_layers=5, E=37, k=3)  # N = 62, W = 6
+    cd = np.random.default_rng(1).uniform(0, 0.5, trees.P.shape).astype(np.float32)
+    S, cnt = m.expand_drafts(trees.parent, to_dev(trees.P), to_dev(trees.F.view(np.int32)), 12.0, 0.4, to_dev(cd))
+    torch.cuda.synchronize()
+    assert np.array_equal(S.cpu().numpy(), oexp.expand_batch(trees.parent, trees.P, trees.F, 12.0, 0.4, cd))
 
 
 @pytest.mark.parametrize("E,T,k", [(128, 5, 8), (128, 20, 8), (300, 7, 3), (8, 4, 2)])
