@@ -199,6 +199,19 @@ def main() -> int:
                          "bytes_per_launch": round(float(kbytes[name].mean())),
                          "GBs": round(float(kbytes[name].sum() / (stage_ms[:, q].sum() * 1e-3) / 1e9), 1)}
     out["kernels"] = kernels
+    # Cost model of the expansion step ([S2-MoE] component 1, Fig. 6): verify
+    # latency = a + T_exp * (unique experts).  Least-squares fit over the
+    # sampled calls (router + gate-up + down kernel time against U).
+    ver_us = (stage_ms[:, 0] + stage_ms[:, 2] + stage_ms[:, 3]) * 1e3
+    u_s = np.array([U[q] + n_sh for q in lidx], dtype=np.float64)
+    if np.ptp(u_s) > 0:
+        b_fit, a_fit = np.polyfit(u_s, ver_us, 1)
+        pred = a_fit + b_fit * u_s
+        r2 = 1.0 - float(((ver_us - pred) ** 2).sum() / ((ver_us - ver_us.mean()) ** 2).sum())
+        out["cost_model"] = {"t_exp_us_per_unique_expert": round(float(b_fit), 3),
+                             "intercept_us": round(float(a_fit), 2), "r2": round(r2, 4),
+                             "mape": round(float(np.mean(np.abs(ver_us - pred) / ver_us)), 4),
+                             "calls": len(lidx), "unique_experts_range": [int(u_s.min()), int(u_s.max())]}
     out["kernel_events"] = f"start/end events on 1 in {EV_STRIDE} verify calls of the timed region ({len(sampled)} calls)"
     out["ffn_us_per_layer"] = round(float(ffn_ms.mean() * 1e3), 2)
     out["ffn_GBs"] = round(float(ffn_bytes.sum() / (ffn_ms.sum() * 1e-3) / 1e9), 1)

@@ -45,10 +45,13 @@ def score(P_t, c: int, eps: float) -> np.float32:
     return np.float32(np.float32(P_t) / (np.float32(c) + np.float32(eps)))
 
 
-def select_drafts(P: np.ndarray, F: np.ndarray, gamma: int, eps: float = 1e-6) -> List[int]:
+def select_drafts(P: np.ndarray, F: np.ndarray, gamma: int, eps: float = 1e-6, static: bool = False) -> List[int]:
     """Greedy cost-aware selection for one tree; returns node ids in pick order.
 
-    P: [N] float32 path probabilities; F: [N, W] uint32 path footprints."""
+    P: [N] float32 path probabilities; F: [N, W] uint32 path footprints.
+    static: the ablation of [EcoSpec] section 4.3, where the cost is the size
+    of the whole path footprint and is not updated by the selection (the
+    buffer B stays empty)."""
     P = np.asarray(P, dtype=np.float32)
     F = np.asarray(F, dtype=np.uint32)
     N = P.shape[0]
@@ -65,13 +68,15 @@ def select_drafts(P: np.ndarray, F: np.ndarray, gamma: int, eps: float = 1e-6) -
             if best_s is None or s > best_s:      # strict: ties keep the lower index
                 best, best_s = t, s
         chosen.append(best)
-        B |= F[best]
+        if not static:
+            B |= F[best]
     return chosen
 
 
-def select_drafts_batch(P: np.ndarray, F: np.ndarray, gamma: int, eps: float = 1e-6) -> np.ndarray:
+def select_drafts_batch(P: np.ndarray, F: np.ndarray, gamma: int, eps: float = 1e-6,
+                        static: bool = False) -> np.ndarray:
     """select_drafts for each of nt trees: P [nt, N], F [nt, N, W] -> [nt, gamma]."""
-    return np.array([select_drafts(P[i], F[i], gamma, eps) for i in range(P.shape[0])],
+    return np.array([select_drafts(P[i], F[i], gamma, eps, static) for i in range(P.shape[0])],
                     dtype=np.int32).reshape(P.shape[0], gamma)
 
 

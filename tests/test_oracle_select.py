@@ -139,3 +139,27 @@ def test_score_is_float32():
             dn = np.nextafter(val, np.float32(-np.inf))
             err = abs(Fraction(float(val)) - exact)
             assert err <= abs(Fraction(float(up)) - exact) and err <= abs(Fraction(float(dn)) - exact)
+
+
+def test_static_cost_is_a_sort_and_agrees_on_disjoint_footprints():
+    rng = np.random.default_rng(31)
+    for _ in range(200):
+        N, nbits = int(rng.integers(1, 12)), int(rng.integers(1, 100))
+        _, P, sets = random_tree_case(rng, N, nbits)
+        gamma = int(rng.integers(0, N + 1))
+        F = sets_to_bits(sets, nbits)
+        got = select.select_drafts(P, F, gamma, static=True)
+        # closed form: top-gamma of P / (|F| + eps), float32, ties to the lower index
+        s = [np.float32(np.float32(P[t]) / (np.float32(len(sets[t])) + np.float32(1e-6))) for t in range(N)]
+        assert got == sorted(range(N), key=lambda t: (-s[t], t))[:gamma]
+    # pairwise disjoint footprints: the marginal cost equals the static one
+    for _ in range(100):
+        N = int(rng.integers(1, 10))
+        sizes = rng.integers(0, 6, N)
+        starts = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+        sets = [set(range(int(a), int(a + b))) for a, b in zip(starts, sizes)]
+        nbits = max(1, int(sizes.sum()))
+        P = rng.uniform(0.05, 1.0, N).astype(np.float32)
+        F = sets_to_bits(sets, nbits)
+        g = int(rng.integers(0, N + 1))
+        assert select.select_drafts(P, F, g, static=True) == select.select_drafts(P, F, g)
