@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--bias", action="store_true", help="turn the reuse-aware soft bias on")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also run the EcoSpec gamma sweep and static-cost ablation (field 'ablation')")
     return ap.parse_args()
 
 
@@ -222,10 +224,68 @@ def main() -> int:
                        "frac": round(gu["GBs"] / HBM_PEAK_GBS, 4),
                        "traffic": measured_traffic(wl.name, "gate_up"),
                        "bytes_per_launch": gu["bytes_per_launch"], "avg_us": gu["avg_us"]}
+    if args.ablation:
+        out["ablation"] = ablation(m, synth, wl, layers, ML, dev, stream)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0
+
+
+def ablation(m, synth, wl, layers, ML, dev, stream, n_trees=8, n_layers=8):
+    """EcoSpec variants on synthetic trees ([EcoSpec] section 4.3): for
+    gamma = 3..6 the drafts chosen by the marginal cost (select_drafts), by
+    the static whole-footprint cost (select_drafts_static) and by confidence
+    alone (the static selection with empty footprints: top-gamma by P) are
+    verified together with the root token, each token routed to its own
+    predicted experts (a perfect predictor), on n_layers of the model's
+    layers; reports the unique experts per layer (from the library) and the
+    verify kernel time per layer (router + gate-up + down events)."""
+    import numpy as np
+    import torch
+    trees = synth.draft_trees(seed=11, nt=n_trees, n_layers=ML, E=wl.E, k=wl.k, rate=wl.rate, with_own=True)
+    P_d = torch.from_numpy(trees.P).to(dev)
+    F_d = torch.from_numpy(trees.F.view(np.int32)).to(dev)
+    Z_d = torch.zeros_like(F_d)
+    rng = synth.rng_for(0, wl.cid, 777)
+    NS = m.NUM_STAGES
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * NS)]
+    for e in evs:
+        e.record(stream)
+    torch.cuda.synchronize()
+    res = {"gamma": [3, 4, 5, 6], "trees": n_trees, "layers": n_layers,
+           "note": "tokens routed to their predicted experts; unique experts and kernel us per layer"}
+    for mode in ("marginal", "static", "confidence"):
+        U_m, us_m = [], []
+        for gamma in res["gamma"]:
+            if mode == "marginal":
+                S = m.select_drafts(trees.parent, P_d, F_d, gamma)
+            else:
+                S = m.select_drafts(trees.parent, P_d, F_d if mode == "static" else Z_d, gamma, static=True)
+            S = S.cpu().numpy()
+            us, uu = [], []
+            for t in range(n_trees):
+                sets = np.concatenate([trees.root_own[t][None], trees.own[t][S[t]]], axis=0)
+                T = sets.shape[0]
+                for j in range(n_layers):
+                    lm = j * ML // n_layers                     # model layer of the footprints
+                    lw, _ = layers[j % len(layers)]             # resident weights
+                    lg = synth.logits_for_sets(rng, sets, lm, wl.E)
+                    x = rng.standard_normal((T, wl.H)).astype(np.float32)
+                    Wr = torch.from_numpy(synth.planted_router(x, lg)).to(dev)
+                    lw2 = m.LayerWeights(H=lw.H, I=lw.I, E=lw.E, k=lw.k, wdtype=lw.wdtype, Wr=Wr, W_gu=lw.W_gu,
+                                         W_d=lw.W_d, s_gu=lw.s_gu, s_d=lw.s_d, Wsh_gu=lw.Wsh_gu, Wsh_d=lw.Wsh_d,
+                                         ssh_gu=lw.ssh_gu, ssh_d=lw.ssh_d)
+                    wsp = m.alloc_workspace(lw2, T, None, device=dev)
+                    m.verify_layer(torch.from_numpy(x).to(dev), lw2, workspace=wsp, events=evs)
+                    torch.cuda.synchronize()
+                    us.append(sum(evs[2 * q].elapsed_time(evs[2 * q + 1]) for q in (0, 2, 3)) * 1e3)
+                    uu.append(int(wsp.aux.union_size.item()))
+            U_m.append(round(float(np.mean(uu)), 2))
+            us_m.append(round(float(np.mean(us)), 1))
+        res[mode] = {"unique_experts_per_layer": U_m, "verify_kernel_us_per_layer": us_m}
+        err(f"[bench] ablation {mode}: U {U_m} us {us_m}")
+    return res
 
 
 KERNEL_SOURCES = ("ffn.hip", "route_block.h", "common.h", "internal.h")

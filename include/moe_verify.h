@@ -189,6 +189,14 @@ int union_stats(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32
 int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred,
                   int32_t W, int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream);
 
+/* Static-cost ablation of the selection ([EcoSpec] section 4.3): the same
+ * greedy loop and arguments as select_drafts, but every node pays the size
+ * of its whole footprint, popcount(F_t), and B is never updated, so the
+ * result is the top-gamma of P_t / (popcount(F_t) + eps) in float32 with
+ * ties to the lower node index. */
+int select_drafts_static(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred, int32_t W,
+                         int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream);
+
 /* Utility-driven adaptive expansion of draft trees ([S2-MoE] component 1,
  * routing-aware adaptive speculative expansion).  Per tree, a draft token i
  * joins the expansion set S while its utility

@@ -9,7 +9,7 @@ Entry points (same names as the C ABI in include/moe_verify.h):
   pack_weights(src, wdtype, gate_up)  -> packed weights (one-time preparation)
   verify_layer(x, layer, bias=None)   -> (y, aux)
   union_stats(topk_idx, E)            -> (counts, reuse)
-  select_drafts(parent, P, Epred, gamma, eps=1e-6) -> S
+  select_drafts(parent, P, Epred, gamma, eps=1e-6, static=False) -> S
   expand_drafts(parent, P, Epred, t_ar, t_exp, c_draft=None) -> (S, count)
   workspace_bytes(layer, T, bias=None)
 """
@@ -30,7 +30,7 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 NUM_STAGES = 5
 STAGE_NAMES = ("router", "route", "gate_up", "down", "combine")
 EXPORTED = ("moe_pack_weights", "moe_verify_workspace_bytes", "moe_verify_layer", "union_stats",
-            "select_drafts", "expand_drafts", "moe_last_error")
+            "select_drafts", "select_drafts_static", "expand_drafts", "moe_last_error")
 
 _vp, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.union_stats.restype = ctypes.c_int
         L.select_drafts.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _vp]
         L.select_drafts.restype = ctypes.c_int
+        L.select_drafts_static.argtypes = L.select_drafts.argtypes
+        L.select_drafts_static.restype = ctypes.c_int
         L.expand_drafts.argtypes = [_vp, _i32, _vp, _vp, _i32, _f32, _f32, _vp, _i32, _vp, _vp, _vp]
         L.expand_drafts.restype = ctypes.c_int
         L.moe_pack_weights.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
@@ -274,10 +276,11 @@ def union_stats(topk_idx, E: int, counts=None, reuse=None, stream=None):
     return counts, reuse
 
 
-def select_drafts(parent, P, Epred, gamma: int, eps: float = 1e-6, out=None, stream=None):
+def select_drafts(parent, P, Epred, gamma: int, eps: float = 1e-6, out=None, stream=None, static: bool = False):
     """EcoSpec greedy selection for nt trees: parent (host) [N], P [nt, N]
     float32 and Epred [nt, N, W] uint32/int32 (device).  Returns S [nt, gamma]
-    int32 (device)."""
+    int32 (device).  static=True runs the static-cost ablation
+    (select_drafts_static)."""
     import torch
     par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
     if P.dtype != torch.float32 or P.dim() != 2 or not P.is_contiguous():
@@ -290,8 +293,8 @@ def select_drafts(parent, P, Epred, gamma: int, eps: float = 1e-6, out=None, str
     W = int(Epred.shape[2])
     S = out if out is not None else torch.empty((nt, gamma), dtype=torch.int32, device=P.device)
     s = stream if stream is not None else torch.cuda.current_stream(P.device).cuda_stream
-    _check(lib().select_drafts(par.ctypes.data, N, P.data_ptr(), Epred.data_ptr(), W, gamma, eps, nt,
-                               S.data_ptr(), s))
+    fn = lib().select_drafts_static if static else lib().select_drafts
+    _check(fn(par.ctypes.data, N, P.data_ptr(), Epred.data_ptr(), W, gamma, eps, nt, S.data_ptr(), s))
     return S
 
 

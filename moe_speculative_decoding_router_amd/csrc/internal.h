@@ -78,7 +78,7 @@ hipError_t launch_pack(const void *src, void *dst, int E, int R, int K, int esz,
 hipError_t launch_union_stats(const int32_t *topk_idx, int nL, int T, int k, int E, int32_t *counts,
                               float *reuse, hipStream_t s);
 hipError_t launch_select(int N, const float *P, const uint32_t *F, int W, int gamma, float eps,
-                         int nt, int32_t *S, hipStream_t s);
+                         int nt, int32_t *S, bool update_b, hipStream_t s);
 
 // Arguments of the expansion kernel (parents by value: no device copy).
 constexpr int kMaxExpandNodes = 1024;

@@ -272,8 +272,8 @@ int union_stats(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32
     return MOE_OK;
 }
 
-int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred, int32_t W,
-                  int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream) {
+static int select_common(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred, int32_t W,
+                  int32_t gamma, float eps, int32_t nt, int32_t *S, bool update_b, void *stream) {
     if (!parent) return fail(MOE_EINVAL, "parent is NULL");
     if (N < 1 || N > 4096) return fail(MOE_EINVAL, "N=%d outside [1, 4096]", N);
     if (W < 1 || W > 4096) return fail(MOE_EINVAL, "W=%d outside [1, 4096]", W);
@@ -288,11 +288,21 @@ int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32
                     moe::kSelectMaxLdsWords);
     if (nt == 0 || gamma == 0) return MOE_OK;  // nothing to write
     if (!P || !Epred || !S) return fail(MOE_EINVAL, "NULL pointer");
-    hipError_t err = moe::launch_select(N, P, Epred, W, gamma, eps, nt, S, static_cast<hipStream_t>(stream));
+    hipError_t err = moe::launch_select(N, P, Epred, W, gamma, eps, nt, S, update_b, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(MOE_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
     return MOE_OK;
 }
 
+
+int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred, int32_t W,
+                  int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream) {
+    return select_common(parent, N, P, Epred, W, gamma, eps, nt, S, true, stream);
+}
+
+int select_drafts_static(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred, int32_t W,
+                         int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream) {
+    return select_common(parent, N, P, Epred, W, gamma, eps, nt, S, false, stream);
+}
 
 int expand_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred, int32_t W, float t_ar,
                   float t_exp, const float *c_draft, int32_t nt, int32_t *S, int32_t *count, void *stream) {

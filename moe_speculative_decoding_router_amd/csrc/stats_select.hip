@@ -46,12 +46,13 @@ __global__ __launch_bounds__(256) void union_stats_kernel(const int32_t *__restr
 // dividing the wave) popcount the words of F & ~B of their nodes and reduce
 // the count inside the group, so every node is scored in parallel; wave 0
 // then takes the arg-max in (score desc, node asc) order and all threads add
-// the chosen footprint to B.
+// the chosen footprint to B (left empty for the static-cost ablation, where
+// every node pays its whole footprint).
 constexpr int kSelThreads = 256;
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(int N, const float *__restrict__ P,
                                                              const uint32_t *__restrict__ F, int W, int gamma,
-                                                             float eps, int nt, int tpn, int32_t *S) {
+                                                             float eps, int nt, int tpn, int update_b, int32_t *S) {
     extern __shared__ uint32_t lds[];
     uint32_t *Fs = lds;                                   // [N * W]
     uint32_t *Bs = Fs + (size_t)N * W;                    // [W]
@@ -120,7 +121,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int N, const float 
         }
         __syncthreads();
         const int best = best_sh;
-        for (int i = tid; i < W; i += kSelThreads) Bs[i] |= Fs[(size_t)best * W + i];
+        if (update_b)  // the static-cost ablation keeps B empty
+            for (int i = tid; i < W; i += kSelThreads) Bs[i] |= Fs[(size_t)best * W + i];
         __syncthreads();
     }
 }
@@ -242,12 +244,13 @@ hipError_t launch_expand(ExpandArgs a, const float *P, const uint32_t *F, const 
 }
 
 hipError_t launch_select(int N, const float *P, const uint32_t *F, int W, int gamma, float eps, int nt,
-                         int32_t *S, hipStream_t s) {
+                         int32_t *S, bool update_b, hipStream_t s) {
     const size_t lds = ((size_t)N * W + W + N + (N + 31) / 32) * 4;
     // threads per node: the largest power of two <= min(64, 256 / N), at least 1
     int tpn = 1;
     while (tpn * 2 <= 64 && tpn * 2 * N <= kSelThreads) tpn *= 2;
-    hipLaunchKernelGGL(select_kernel, dim3(nt), dim3(kSelThreads), lds, s, N, P, F, W, gamma, eps, nt, tpn, S);
+    hipLaunchKernelGGL(select_kernel, dim3(nt), dim3(kSelThreads), lds, s, N, P, F, W, gamma, eps, nt, tpn,
+                       update_b ? 1 : 0, S);
     return hipGetLastError();
 }
 

@@ -285,6 +285,8 @@ class DraftTrees:
     n_layers: int
     E: int
     k: int
+    own: Optional[np.ndarray] = None        # [nt, N, W] each node's own per-layer experts
+    root_own: Optional[np.ndarray] = None   # [nt, W] the root token's per-layer experts
 
 
 def tree_parents(depth: int, branch: int) -> np.ndarray:
@@ -304,7 +306,7 @@ def tree_parents(depth: int, branch: int) -> np.ndarray:
 
 def draft_trees(seed: int, nt: int, depth: int = 3, branch: int = 2, n_layers: int = 36,
                 E: int = 128, k: int = 4, rate: float = 0.05, p_lo: float = 0.3,
-                stream: int = 0, chunk: int = 256) -> DraftTrees:
+                stream: int = 0, chunk: int = 256, with_own: bool = False) -> DraftTrees:
     """Batch of nt draft trees.
 
     Each node draws its own per-layer set of k distinct experts, sampled
@@ -313,12 +315,17 @@ def draft_trees(seed: int, nt: int, depth: int = 3, branch: int = 2, n_layers: i
     correlated through the shared per-tree context.  A node's footprint is
     the union of its own sets and those of its ancestors, the root excluded.
     Edge probabilities are U(p_lo, 1); P is their running product in
-    float32 (so P(child) <= P(parent))."""
+    float32 (so P(child) <= P(parent)).  with_own also returns each node's
+    own sets and a root token's sets (same model and tree context, drawn from
+    a separate stream, so the trees themselves do not change)."""
     parent = tree_parents(depth, branch)
     N = len(parent)
     W = (n_layers * E + 31) // 32
     P = np.empty((nt, N), dtype=np.float32)
     F = np.zeros((nt, N, W), dtype=np.uint32)
+    OWN = np.zeros((nt, N, W), dtype=np.uint32) if with_own else None
+    ROOT = np.zeros((nt, W), dtype=np.uint32) if with_own else None
+    rng_root = rng_for(seed, 3, stream, 1) if with_own else None
     rng = rng_for(seed, 3, stream)
     rank = rng.permutation(E).astype(np.float64)
     pop = 1.5 * np.exp(-rate * rank)
@@ -343,7 +350,27 @@ def draft_trees(seed: int, nt: int, depth: int = 3, branch: int = 2, n_layers: i
                 bits[:, i] = own[:, i] | bits[:, pi]
                 P[c0:c0 + c, i] = (P[c0:c0 + c, pi] * edge[:, i]).astype(np.float32)
         F[c0:c0 + c] = pack_bits(bits, W)
-    return DraftTrees(parent=parent, P=P, F=F, n_layers=n_layers, E=E, k=k)
+        if with_own:
+            OWN[c0:c0 + c] = pack_bits(own, W)
+            rk = pop + ctx[:, 0] + 0.7 * rng_root.standard_normal((c, n_layers, E)) \
+                - np.log(-np.log(rng_root.uniform(1e-300, 1.0, size=(c, n_layers, E))))
+            rsel = np.argpartition(-rk, k - 1, axis=-1)[..., :k]
+            rbits = np.zeros((c, n_layers, E), dtype=bool)
+            np.put_along_axis(rbits, rsel, True, axis=-1)
+            ROOT[c0:c0 + c] = pack_bits(rbits.reshape(c, n_layers * E), W)
+    return DraftTrees(parent=parent, P=P, F=F, n_layers=n_layers, E=E, k=k, own=OWN, root_own=ROOT)
+
+
+def logits_for_sets(rng: np.random.Generator, sets: np.ndarray, layer: int, E: int) -> np.ndarray:
+    """Router logits [T, E] whose per-token top sets are given: row t has
+    values 10 + U(0, 1) on the experts of bit row sets[t] at `layer` (bits
+    layer * E .. layer * E + E - 1 of the packed words) and 0.1 * N(0, 1)
+    elsewhere, so the top-|set| of each row is exactly its set."""
+    T = sets.shape[0]
+    bits = np.unpackbits(sets.view(np.uint8), axis=-1, bitorder="little")[:, layer * E:(layer + 1) * E].astype(bool)
+    out = 0.1 * rng.standard_normal((T, E))
+    out[bits] = 10.0 + rng.uniform(0.0, 1.0, int(bits.sum()))
+    return out
 
 
 def pack_bits(bits: np.ndarray, W: int) -> np.ndarray:

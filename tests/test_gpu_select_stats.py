@@ -18,8 +18,8 @@ import moe_speculative_decoding_router_amd as m  # noqa: E402
 from gpu_helpers import log, to_dev  # noqa: E402
 
 
-def run_select(trees, gamma, eps=1e-6):
-    S = m.select_drafts(trees.parent, to_dev(trees.P), to_dev(trees.F.view(np.int32)), gamma, eps)
+def run_select(trees, gamma, eps=1e-6, static=False):
+    S = m.select_drafts(trees.parent, to_dev(trees.P), to_dev(trees.F.view(np.int32)), gamma, eps, static=static)
     torch.cuda.synchronize()
     return S.cpu().numpy()
 
@@ -31,6 +31,14 @@ def test_select_gptoss_trees(gamma):
     S = run_select(trees, gamma)
     ref = osel.select_drafts_batch(trees.P, trees.F, gamma)
     assert np.array_equal(S, ref)
+
+
+@pytest.mark.parametrize("gamma", [1, 4, 6])
+def test_select_static_cost(gamma):
+    log(f"case select_drafts_static gptoss trees nt=128 gamma={gamma}")
+    trees = synth.draft_trees(seed=0, nt=128, n_layers=36, E=128, k=4)
+    S = run_select(trees, gamma, static=True)
+    assert np.array_equal(S, osel.select_drafts_batch(trees.P, trees.F, gamma, static=True))
 
 
 def test_select_ties_and_odd_widths():

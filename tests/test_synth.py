@@ -83,3 +83,24 @@ def test_draft_trees_structure():
     depth = np.array([1, 1, 2, 2, 2, 2, 3, 3, 3, 3, 3, 3, 3, 3])
     pc = np.unpackbits(tr.F.view(np.uint8), axis=-1).sum(-1)
     assert np.all(pc <= depth[None] * 36 * 4) and np.all(pc >= 36 * 4)
+
+
+def test_tree_own_sets_and_logits_for_sets():
+    a = synth.draft_trees(seed=0, nt=5, n_layers=4, E=16, k=2)
+    b = synth.draft_trees(seed=0, nt=5, n_layers=4, E=16, k=2, with_own=True)
+    assert np.array_equal(a.F, b.F) and np.array_equal(a.P, b.P)      # the trees do not change
+
+    def per_layer(bits):
+        return np.unpackbits(bits.view(np.uint8), bitorder="little")[:64].reshape(4, 16)
+    rng = np.random.default_rng(0)
+    for t in range(5):
+        assert (per_layer(b.root_own[t]).sum(1) == 2).all()
+        for i, pi in enumerate(b.parent):
+            assert (per_layer(b.own[t, i]).sum(1) == 2).all()
+            assert np.array_equal(b.F[t, i], b.own[t, i] | (b.F[t, pi] if pi >= 0 else 0))
+        sets = np.concatenate([b.root_own[t][None], b.own[t]], axis=0)
+        for layer in range(4):
+            lg = synth.logits_for_sets(rng, sets, layer, 16)
+            top = np.argsort(-lg, axis=1)[:, :2]
+            for r in range(sets.shape[0]):
+                assert set(top[r].tolist()) == set(np.nonzero(per_layer(sets[r])[layer])[0].tolist())
