@@ -16,6 +16,8 @@ docstrings:
               per-layer union statistics;
 * ``select``  EcoSpec cost-aware greedy draft selection;
 * ``expand``  S^2-MoE utility-driven adaptive expansion of a draft tree;
+* ``ragged``  confidence-gated per-sequence depths and per-sequence union
+              statistics of a ragged verify call;
 * ``fp``      bf16 and OCP FP8 E4M3FN decoding from their definitions.
 
 Parity status: every function is pinned by CPU tests against closed forms,
@@ -24,4 +26,4 @@ of the reuse-bias steps (importance g, TopCap, bias size), whose formulas are
 missing from the page; that part is pinned to the stated reading and to the
 page's qualitative example only ("parity pinned to the reading").
 """
-from . import expand, fp, moe, select  # noqa: F401
+from . import expand, fp, moe, ragged, select  # noqa: F401
