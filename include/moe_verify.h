@@ -189,6 +189,36 @@ int union_stats(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32
 int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred,
                   int32_t W, int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream);
 
+/* Per-sequence unique experts of a ragged verify call ([W-vs-D] section 2,
+ * ragged speculation: sequences verify different numbers of tokens in one
+ * call).  The T tokens of the call are grouped by sequence: rows
+ * offsets[s] .. offsets[s+1]-1 belong to sequence s.
+ *   topk_idx [nL, T, k] int32 (device), entries outside [0, E) ignored
+ *   offsets  (host) [S + 1] int32, 0 = offsets[0] <= ... <= offsets[S] = T
+ *   per      [nL, S] int32 out: distinct experts of each sequence's tokens
+ *   total    [nL] int32 out: distinct experts of the whole call
+ * Limits: 1 <= S <= 64.  Errors: EINVAL (NULL, shapes, offsets). */
+int union_stats_segments(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32_t E,
+                         const int32_t *offsets, int32_t S, int32_t *per, int32_t *total, void *stream);
+
+/* Confidence-gated per-sequence depths ([W-vs-D] section 2): one batch-wide
+ * depth, then greedy per-sequence truncation, maximising the expected
+ * throughput
+ *     sum_s (1 + c[s,1] + ... + c[s,d_s]) / (t_base + t_exp * U(d)),
+ * where U(d) is the number of distinct (layer, expert) pairs over every
+ * verified token (the root j = 0 and drafts 1..d_s of each sequence).  The
+ * batch-wide depth is the smallest D in 0..Dmax with the largest throughput;
+ * then, for s = 0..S-1 in order, d_s is lowered one step at a time while that
+ * raises the throughput strictly.  Float32 as fl(total / fl(t_base +
+ * fl(t_exp * U))) with A_s summed over j ascending and the total over s
+ * ascending.
+ *   c     [S, Dmax + 1] float32 cumulative draft confidences (column 0 unused)
+ *   Epred [S, Dmax + 1, W] uint32 expert bitsets of each token
+ *   d     [S] int32 out: the depths
+ * Limits: S <= 64, Dmax <= 64, W <= 1024.  Errors: EINVAL. */
+int gate_depths(const float *c, const uint32_t *Epred, int32_t S, int32_t Dmax, int32_t W, float t_base,
+                float t_exp, int32_t *d, void *stream);
+
 /* Static-cost ablation of the selection ([EcoSpec] section 4.3): the same
  * greedy loop and arguments as select_drafts, but every node pays the size
  * of its whole footprint, popcount(F_t), and B is never updated, so the

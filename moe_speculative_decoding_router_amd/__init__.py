@@ -11,6 +11,8 @@ Entry points (same names as the C ABI in include/moe_verify.h):
   union_stats(topk_idx, E)            -> (counts, reuse)
   select_drafts(parent, P, Epred, gamma, eps=1e-6, static=False) -> S
   expand_drafts(parent, P, Epred, t_ar, t_exp, c_draft=None) -> (S, count)
+  union_stats_segments(topk_idx, E, offsets) -> (per, total)
+  gate_depths(c, Epred, t_base, t_exp) -> d
   workspace_bytes(layer, T, bias=None)
 """
 from __future__ import annotations
@@ -30,7 +32,8 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 NUM_STAGES = 5
 STAGE_NAMES = ("router", "route", "gate_up", "down", "combine")
 EXPORTED = ("moe_pack_weights", "moe_verify_workspace_bytes", "moe_verify_layer", "union_stats",
-            "select_drafts", "select_drafts_static", "expand_drafts", "moe_last_error")
+            "select_drafts", "select_drafts_static", "expand_drafts", "union_stats_segments", "gate_depths",
+            "moe_last_error")
 
 _vp, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 
@@ -75,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.select_drafts_static.restype = ctypes.c_int
         L.expand_drafts.argtypes = [_vp, _i32, _vp, _vp, _i32, _f32, _f32, _vp, _i32, _vp, _vp, _vp]
         L.expand_drafts.restype = ctypes.c_int
+        L.union_stats_segments.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp]
+        L.union_stats_segments.restype = ctypes.c_int
+        L.gate_depths.argtypes = [_vp, _vp, _i32, _i32, _i32, _f32, _f32, _vp, _vp]
+        L.gate_depths.restype = ctypes.c_int
         L.moe_pack_weights.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
         L.moe_pack_weights.restype = ctypes.c_int
         L.moe_last_error.argtypes = []
@@ -323,3 +330,40 @@ def expand_drafts(parent, P, Epred, t_ar: float, t_exp: float, c_draft=None, str
                                c_draft.data_ptr() if c_draft is not None else None, nt, S.data_ptr(),
                                count.data_ptr(), s))
     return S, count
+
+
+def union_stats_segments(topk_idx, E: int, offsets, stream=None):
+    """Per-sequence unique experts of a call grouped by sequence:
+    topk_idx [nL, T, k] int32 (device), offsets (host) [S + 1].  Returns
+    (per [nL, S] int32, total [nL] int32) on the device."""
+    import torch
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int32))
+    if topk_idx.dtype != torch.int32 or topk_idx.dim() != 3 or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be a contiguous int32 [nL, T, k] tensor")
+    nL, T, k = (int(v) for v in topk_idx.shape)
+    S = int(off.shape[0]) - 1
+    per = torch.empty((nL, S), dtype=torch.int32, device=topk_idx.device)
+    total = torch.empty((nL,), dtype=torch.int32, device=topk_idx.device)
+    s = stream if stream is not None else torch.cuda.current_stream(topk_idx.device).cuda_stream
+    _check(lib().union_stats_segments(topk_idx.data_ptr(), nL, T, k, E, off.ctypes.data, S, per.data_ptr(),
+                                      total.data_ptr(), s))
+    return per, total
+
+
+def gate_depths(c, Epred, t_base: float, t_exp: float, stream=None):
+    """Confidence-gated depths: c [S, Dmax + 1] float32 cumulative confidences
+    and Epred [S, Dmax + 1, W] 32-bit expert bitsets (device).  Returns d [S]
+    int32 (device)."""
+    import torch
+    if c.dtype != torch.float32 or c.dim() != 2 or not c.is_contiguous():
+        raise ValueError("c must be a contiguous float32 [S, Dmax + 1] tensor")
+    if Epred.dim() != 3 or Epred.element_size() != 4 or not Epred.is_contiguous():
+        raise ValueError("Epred must be a contiguous 32-bit [S, Dmax + 1, W] tensor")
+    S, D1 = (int(v) for v in c.shape)
+    if tuple(Epred.shape[:2]) != (S, D1):
+        raise ValueError("shape mismatch between c and Epred")
+    d = torch.empty((S,), dtype=torch.int32, device=c.device)
+    s = stream if stream is not None else torch.cuda.current_stream(c.device).cuda_stream
+    _check(lib().gate_depths(c.data_ptr(), Epred.data_ptr(), S, D1 - 1, int(Epred.shape[2]), t_base, t_exp,
+                             d.data_ptr(), s))
+    return d

@@ -91,6 +91,21 @@ size_t expand_lds_bytes(int N, int W);
 hipError_t launch_expand(ExpandArgs a, const float *P, const uint32_t *F, const float *Cd, int32_t *S,
                          int32_t *count, hipStream_t s);
 
+// Ragged verify: segment offsets by value, depth gating limits.
+constexpr int kMaxSegments = 64;
+constexpr int kGateMaxSeq = 64;
+constexpr int kGateMaxDepth = 64;
+constexpr int kGateMaxWords = 1024;  // (layer, expert) pairs <= 32768: 64 KB of uint16 counters
+struct SegmentArgs {
+    int S;
+    int off[kMaxSegments + 1];
+};
+hipError_t launch_segment_stats(const int32_t *topk_idx, int nL, int T, int k, int E, const SegmentArgs &a,
+                                int32_t *per, int32_t *total, hipStream_t s);
+size_t gate_lds_bytes(int W);
+hipError_t launch_gate_depths(const float *c, const uint32_t *Ep, int S, int Dmax, int W, float t_base,
+                              float t_exp, int32_t *d, hipStream_t s);
+
 // Limits used by the kernels.
 constexpr int kMaxTokens = 64;
 constexpr int kMaxExperts = 512;

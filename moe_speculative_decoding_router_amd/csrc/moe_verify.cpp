@@ -333,4 +333,39 @@ int expand_drafts(const int32_t *parent, int32_t N, const float *P, const uint32
     return MOE_OK;
 }
 
+
+int union_stats_segments(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32_t E,
+                         const int32_t *offsets, int32_t S, int32_t *per, int32_t *total, void *stream) {
+    if (!offsets) return fail(MOE_EINVAL, "offsets is NULL");
+    if (nL < 0 || T < 1 || k < 1) return fail(MOE_EINVAL, "need nL >= 0, T >= 1, k >= 1");
+    if (E < 1 || E > 65536) return fail(MOE_EINVAL, "E=%d outside [1, 65536]", E);
+    if (S < 1 || S > moe::kMaxSegments) return fail(MOE_EINVAL, "S=%d outside [1, %d]", S, moe::kMaxSegments);
+    moe::SegmentArgs a{};
+    a.S = S;
+    if (offsets[0] != 0 || offsets[S] != T) return fail(MOE_EINVAL, "offsets must run from 0 to T=%d", T);
+    for (int s = 0; s <= S; ++s) {
+        if (s > 0 && offsets[s] < offsets[s - 1]) return fail(MOE_EINVAL, "offsets must not decrease");
+        a.off[s] = offsets[s];
+    }
+    if (nL == 0) return MOE_OK;
+    if (!topk_idx || !per || !total) return fail(MOE_EINVAL, "NULL pointer");
+    hipError_t err = moe::launch_segment_stats(topk_idx, nL, T, k, E, a, per, total, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(MOE_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return MOE_OK;
+}
+
+int gate_depths(const float *c, const uint32_t *Epred, int32_t S, int32_t Dmax, int32_t W, float t_base,
+                float t_exp, int32_t *d, void *stream) {
+    if (S < 1 || S > moe::kGateMaxSeq) return fail(MOE_EINVAL, "S=%d outside [1, %d]", S, moe::kGateMaxSeq);
+    if (Dmax < 0 || Dmax > moe::kGateMaxDepth)
+        return fail(MOE_EINVAL, "Dmax=%d outside [0, %d]", Dmax, moe::kGateMaxDepth);
+    if (W < 1 || W > moe::kGateMaxWords) return fail(MOE_EINVAL, "W=%d outside [1, %d]", W, moe::kGateMaxWords);
+    if (!std::isfinite(t_base) || !std::isfinite(t_exp) || !(t_base > 0.f) || t_exp < 0.f)
+        return fail(MOE_EINVAL, "need t_base > 0 and t_exp >= 0, finite");
+    if (!c || !Epred || !d) return fail(MOE_EINVAL, "NULL pointer");
+    hipError_t err = moe::launch_gate_depths(c, Epred, S, Dmax, W, t_base, t_exp, d, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(MOE_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return MOE_OK;
+}
+
 }  // extern "C"

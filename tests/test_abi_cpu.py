@@ -124,3 +124,18 @@ def test_expert_bytes_matches_page_figures():
     q = g["table2_qwen_delta"]
     delta_gb = q["experts_delta"] * q["n_layers"] * m.expert_bytes(q["H"], q["I"], "bf16") / 1e9
     assert abs(delta_gb - q["page_delta_GB"]) / q["page_delta_GB"] < q["rel_tol"]
+
+
+def test_ragged_validation(lib):
+    off = np.array([0, 2, 5], dtype=np.int32)
+    assert lib.union_stats_segments(16, 1, 5, 4, 128, None, 2, 16, 16, None) == -1          # offsets NULL
+    assert lib.union_stats_segments(16, 1, 6, 4, 128, off.ctypes.data, 2, 16, 16, None) == -1  # end != T
+    bad = np.array([0, 3, 2, 5], dtype=np.int32)
+    assert lib.union_stats_segments(16, 1, 5, 4, 128, bad.ctypes.data, 3, 16, 16, None) == -1  # decreasing
+    assert lib.union_stats_segments(16, 0, 5, 4, 128, off.ctypes.data, 2, 16, 16, None) == 0   # nothing to do
+    assert lib.gate_depths(16, 16, 0, 4, 8, 1.0, 1.0, 16, None) == -1       # S = 0
+    assert lib.gate_depths(16, 16, 65, 4, 8, 1.0, 1.0, 16, None) == -1      # S > 64
+    assert lib.gate_depths(16, 16, 4, 65, 8, 1.0, 1.0, 16, None) == -1      # Dmax > 64
+    assert lib.gate_depths(16, 16, 4, 4, 1025, 1.0, 1.0, 16, None) == -1    # W > 1024
+    assert lib.gate_depths(16, 16, 4, 4, 8, 0.0, 1.0, 16, None) == -1       # t_base <= 0
+    assert lib.gate_depths(None, 16, 4, 4, 8, 1.0, 1.0, 16, None) == -1     # NULL

@@ -6,6 +6,7 @@ import pytest
 import synth
 from oracle import expand as oexp
 from oracle import moe as omoe
+from oracle import ragged as orag
 from oracle import select as osel
 
 pytestmark = pytest.mark.gpu
@@ -92,6 +93,41 @@ def test_expand_odd_shapes():
     S, cnt = m.expand_drafts(trees.parent, to_dev(trees.P), to_dev(trees.F.view(np.int32)), 12.0, 0.4, to_dev(cd))
     torch.cuda.synchronize()
     assert np.array_equal(S.cpu().numpy(), oexp.expand_batch(trees.parent, trees.P, trees.F, 12.0, 0.4, cd))
+
+
+def chains(seed, S, Dmax, n_layers, E, k):
+    """S sequences of Dmax chained drafts: cumulative confidences and the
+    expert bitsets of each sequence's root and drafts."""
+    tr = synth.draft_trees(seed=seed, nt=S, depth=Dmax, branch=1, n_layers=n_layers, E=E, k=k, with_own=True)
+    c = np.concatenate([np.ones((S, 1), np.float32), tr.P], axis=1)
+    Ep = np.concatenate([tr.root_own[:, None], tr.own], axis=1)
+    return c, Ep
+
+
+@pytest.mark.parametrize("S,Dmax,t_base,t_exp", [(4, 8, 400.0, 1.0), (16, 6, 200.0, 0.5), (64, 4, 1000.0, 1.0),
+                                                 (8, 12, 50.0, 0.05), (3, 0, 10.0, 1.0), (5, 5, 100.0, 0.0)])
+def test_gate_depths(S, Dmax, t_base, t_exp):
+    log(f"case gate_depths S={S} Dmax={Dmax} t_base={t_base} t_exp={t_exp}")
+    c, Ep = chains(S + 31 * Dmax, S, Dmax, 36, 128, 4)
+    d = m.gate_depths(to_dev(c), to_dev(Ep.view(np.int32)), t_base, t_exp)
+    torch.cuda.synchronize()
+    ref = orag.gate_depths(c, Ep, t_base, t_exp)
+    assert d.cpu().numpy().tolist() == ref
+    log(f"    depths {ref}")
+
+
+def test_union_stats_segments():
+    log("case union_stats_segments")
+    rng = np.random.default_rng(12)
+    E, k, nL = 128, 8, 12
+    off = np.array([0, 5, 6, 6, 14, 20], dtype=np.int32)           # ragged, one empty segment
+    T = int(off[-1])
+    L = np.stack([synth.structured_logits(rng, 1, T, E, 0.05) for _ in range(nL)]).astype(np.float32)
+    idx = np.stack([omoe.topk(L[l], k) for l in range(nL)]).astype(np.int32)
+    per, tot = m.union_stats_segments(to_dev(idx), E, off)
+    torch.cuda.synchronize()
+    rp, rt = orag.segment_union_stats(idx, off, E)
+    assert np.array_equal(per.cpu().numpy(), rp) and np.array_equal(tot.cpu().numpy(), rt)
 
 
 @pytest.mark.parametrize("E,T,k", [(128, 5, 8), (128, 20, 8), (300, 7, 3), (8, 4, 2)])
