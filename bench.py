@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--bias", action="store_true", help="turn the reuse-aware soft bias on")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the workload, copy this many MiB device to device once (a plain copy of "
+                         "known size, the calibration of the HBM byte counters)")
     ap.add_argument("--ablation", action="store_true",
                     help="also run the EcoSpec gamma sweep and static-cost ablation (field 'ablation')")
     return ap.parse_args()
@@ -56,7 +59,7 @@ def parse():
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the path has no multi-GPU code); got --gpus {args.gpus}",
               file=sys.stderr)
         return 2
     import numpy as np
@@ -71,6 +74,16 @@ def main() -> int:
 
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if args.copy_probe_mib > 0:
+        nb = args.copy_probe_mib << 20
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        err(f"[bench] copy probe: {nb} bytes device to device")
+        del src, dst
 
     # ---------------- inputs (seeded, synthetic, resident in HBM) ----------------
     err(f"[bench] building {L} {wl.name} layers on the device")
@@ -303,8 +316,8 @@ def kernel_source_digest():
 
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary of
-    this workload (FETCH_SIZE and WRITE_SIZE scaled by the pack kernel, a
-    plain permutation copy of known size, in the same runs), or None when the
+    this workload (FETCH_SIZE and WRITE_SIZE scaled by what they count for a
+    plain device-to-device copy of known size in the same runs), or None when the
     summary is missing or the kernel source changed since the counters were
     taken."""
     path = os.path.join(ROOT, "profiles", f"pmc_{workload}.md")
