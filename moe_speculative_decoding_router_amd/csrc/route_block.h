@@ -25,6 +25,7 @@ namespace moe {
 
 constexpr int kRouteNJ = kMaxExperts / 64;  // row entries per lane
 constexpr int kRankSlots = kMaxTopK + 1;    // k, or k + 1 when the bias needs l_(k+1)
+constexpr int kTokWords = kMaxExperts / 32;  // words of a token's expert bitset
 
 __device__ __forceinline__ float nan_to_ninf(float v) { return v != v ? -INFINITY : v; }
 
@@ -34,6 +35,62 @@ __device__ __forceinline__ unsigned float_ord(float x) {
     unsigned u = __float_as_uint(x);
     if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of float_ord (-0 comes back as +0).
+__device__ __forceinline__ float ord_float(unsigned k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Unsigned maximum over the wave: DPP row rotations, then the four row
+// results; uniform.
+__device__ __forceinline__ unsigned wave_umax(unsigned v) {
+    int x = (int)v;
+    x = (int)max((unsigned)x, (unsigned)dpp_ror<8>(x));
+    x = (int)max((unsigned)x, (unsigned)dpp_ror<4>(x));
+    x = (int)max((unsigned)x, (unsigned)dpp_ror<2>(x));
+    x = (int)max((unsigned)x, (unsigned)dpp_ror<1>(x));
+    const unsigned r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+    const unsigned r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Rank order by repeated maxima: round r takes the largest key left and, among
+// the entries that hold it, the lowest index, and retires that entry.  Keys
+// are float_ord images (entry lane + 64 j in key[j]); invalid entries hold 0,
+// below the image of every non-NaN float.  Lane r < K receives rank r (index
+// returned, key in *rkey); the keys are consumed.  Each round is one short
+// chain of row rotations and ballots, so for small K this beats the radix
+// search and needs no ranking pass.
+constexpr int kRoundsMaxK = 16;
+
+template <int NJ>
+__device__ __forceinline__ int wave_topk_rounds(unsigned (&key)[kRouteNJ], int K, unsigned *rkey) {
+    const int lane = threadIdx.x & 63;
+    int mine = 0;
+    unsigned mk = 0u;
+    for (int r = 0; r < K; ++r) {
+        unsigned lm = key[0];
+#pragma unroll
+        for (int j = 1; j < NJ; ++j) lm = max(lm, key[j]);
+        const unsigned M = wave_umax(lm);
+        int idx = 0;
+#pragma unroll
+        for (int j = NJ - 1; j >= 0; --j) {
+            const unsigned long long b = __ballot(key[j] == M);
+            if (b) idx = 64 * j + (int)__builtin_ctzll(b);
+        }
+        idx = __builtin_amdgcn_readfirstlane(idx);
+        if (lane == r) {
+            mine = idx;
+            mk = M;
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            if (lane + 64 * j == idx) key[j] = 0u;
+    }
+    *rkey = mk;
+    return mine;
 }
 
 // Row of E logits into registers, entry lane + 64 j in v[j]; entries past E
@@ -136,11 +193,44 @@ __device__ __forceinline__ RankEntry wave_rank(unsigned sel, const unsigned (&ke
     return out;
 }
 
+// Lane r < K receives the entry of rank r (value desc, index asc) among the
+// valid entries of a row (entry lane + 64 j in slot j; bit j of `valid`);
+// v is ranked, v2 is carried along when `carry` (else v2 = v).  Repeated
+// maxima for K <= kRoundsMaxK, else the radix search and a ranking pass.
+template <int NJ>
+__device__ __forceinline__ RankEntry wave_select(const float (&v)[kRouteNJ], const float (&v2)[kRouteNJ],
+                                                 unsigned valid, int K, RankEntry *rbuf, bool carry) {
+    const int lane = threadIdx.x & 63;
+    unsigned key[kRouteNJ];
+#pragma unroll
+    for (int j = 0; j < kRouteNJ; ++j) key[j] = ((valid >> j) & 1u) ? float_ord(v[j]) : 0u;
+    if (K <= kRoundsMaxK) {
+        unsigned mk;
+        const int idx = wave_topk_rounds<NJ>(key, K, &mk);
+        const float val = ord_float(mk);
+        float c = val;
+        if (carry) {
+            // the carried value of the selected entry, from the lane holding it
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float o = __shfl(v2[j], idx & 63);
+                if ((idx >> 6) == j) c = o;
+            }
+        }
+        RankEntry out{0u, 0, -INFINITY, -INFINITY};
+        if (lane < K) out = RankEntry{mk, idx, val, c};
+        return out;
+    }
+    const unsigned sel = wave_topk_mask<NJ>(key, valid, K);
+    return wave_rank<NJ>(sel, key, v, v2, K, rbuf);
+}
+
 // LDS scratch of block_route, carved from a byte buffer for runtime T, k, E.
 struct RouteScratch {
     RankEntry *rank;            // [waves * 2 * kRankSlots]
-    unsigned long long *tmask;  // [E] tokens routed to each expert
-    unsigned long long *tmask0; // [E] first-pass membership (bias only)
+    unsigned long long *tmask;  // [E] tokens routed to each expert (union members)
+    unsigned *tbits;            // [T * kTokWords] experts of each token, one bit each
+    unsigned *tbits0;           // [T * kTokWords] first-pass experts of each token (bias only)
     int *sel_i;                 // [T * k] first-pass selection (bias only)
     float *cg;                  // [T * k] w_b * softmax(l_b)_e of the selected e
     int *fin_i;                 // [T * k] final selection
@@ -152,8 +242,8 @@ struct RouteScratch {
     int *misc;                  // [4]: U, |P*|
 
     __host__ __device__ static size_t bytes(int T, int k, int E, int waves) {
-        return (size_t)waves * 2 * kRankSlots * sizeof(RankEntry) + (size_t)E * 16 + (size_t)T * k * 16 +
-               (size_t)E * 8 + (size_t)T * 4 + (size_t)(2 * waves + 4) * 4 + 64;
+        return (size_t)waves * 2 * kRankSlots * sizeof(RankEntry) + (size_t)E * 8 + (size_t)T * kTokWords * 8 +
+               (size_t)T * k * 16 + (size_t)E * 8 + (size_t)T * 4 + (size_t)(2 * waves + 4) * 4 + 64;
     }
     __device__ void carve(unsigned char *base, int T, int k, int E, int waves) {
         unsigned char *q = base;
@@ -161,8 +251,10 @@ struct RouteScratch {
         q += (size_t)waves * 2 * kRankSlots * sizeof(RankEntry);
         tmask = reinterpret_cast<unsigned long long *>(q);
         q += (size_t)E * 8;
-        tmask0 = reinterpret_cast<unsigned long long *>(q);
-        q += (size_t)E * 8;
+        tbits = reinterpret_cast<unsigned *>(q);
+        q += (size_t)T * kTokWords * 4;
+        tbits0 = reinterpret_cast<unsigned *>(q);
+        q += (size_t)T * kTokWords * 4;
         sel_i = reinterpret_cast<int *>(q);
         q += (size_t)T * k * 4;
         cg = reinterpret_cast<float *>(q);
@@ -190,8 +282,9 @@ struct RouteScratch {
 //        meta, the slot tables (slot_expert, tokw, tokpos, tpos) of the FFN
 //        kernels.
 // The first pass gives token t to wave t % (NTHREADS / 64); waves without a
-// token go straight to the first barrier (the caller may hand them other
-// work before the call).
+// token wait at the barrier that ends it (the caller may hand them other work
+// before the call).  Barriers: pass 1, [bias: importance, preferred set,
+// re-selection], union scan, tables.
 // NJ: row entries per lane the selections scan (>= ceil(E / 64)).
 template <int NTHREADS, int NJ>
 __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned char *scratch, int *sexp, float *tw,
@@ -209,34 +302,41 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     for (int j = 0; j < kRouteNJ; ++j)
         if (lane + 64 * j < E) valid |= 1u << j;
 
-    // zeroing needs no barrier of its own: the first pass does not touch it
-    for (int e = tid; e < E; e += NTHREADS) {
-        sh.tmask[e] = 0ull;
-        sh.tmask0[e] = 0ull;
-        sh.inP[e] = 0;
-    }
+    // A token's experts go to its bitset row (lane L writes word L, so every
+    // word is written once and nothing needs clearing); the per-expert token
+    // masks are assembled from the rows after the selections.
+    auto put_bits = [&](unsigned *rows, int t, int idx, int K) {
+        unsigned word = 0u;
+        for (int r = 0; r < K; ++r) {
+            const int e = __builtin_amdgcn_readlane(idx, r);
+            if ((e >> 5) == lane) word |= 1u << (e & 31);
+        }
+        if (lane < kTokWords) rows[t * kTokWords + lane] = word;
+    };
 
     // ---- pass 1: top-k (k + 1 when the bias needs the (k+1)-th logit);
     //      lane r ends with the entry of rank r ----
     const int R = (bias && k < E) ? k + 1 : k;
     for (int t = w; t < T; t += NW) {
         float v[kRouteNJ];
-        unsigned key[kRouteNJ];
         load_logits(p.logits + (size_t)t * E, E, v);
         const float wc = bias ? p.w_conf[t] : 0.f;
-#pragma unroll
-        for (int j = 0; j < kRouteNJ; ++j) key[j] = float_ord(v[j]);
-        const unsigned sel = wave_topk_mask<NJ>(key, valid, R);
-        const RankEntry me = wave_rank<NJ>(sel, key, v, v, R, rbuf);
+        const RankEntry me = wave_select<NJ>(v, v, valid, R, rbuf, false);
         const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(me.v), 0));
         const bool mine = lane < k;
         if (!bias) {
             const float ex = mine ? expf(me.v - m) : 0.f;
             const float s = wave_sum(ex);
             if (mine) {
+                const float wt = ex / s;
                 sh.fin_i[t * k + lane] = me.idx;
-                sh.fin_w[t * k + lane] = ex / s;
+                sh.fin_w[t * k + lane] = wt;
+                if (write_global) {
+                    p.topk_idx[t * k + lane] = me.idx;
+                    p.topk_w[t * k + lane] = wt;
+                }
             }
+            put_bits(sh.tbits, t, me.idx, k);
         } else {
             // softmax over all E for the importance aggregation (R4)
             float z = 0.f;
@@ -248,6 +348,7 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
                 sh.sel_i[t * k + lane] = me.idx;
                 sh.cg[t * k + lane] = wc * (expf(me.v - m) / z);
             }
+            put_bits(sh.tbits0, t, me.idx, k);
             // lambda_b = alpha * (l_(1) - l_(k+1)), float32, no contraction (R6)
             if (k < E) {
                 const float vk1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(me.v), k));
@@ -260,21 +361,16 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     lds_barrier();
 
     if (bias) {
-        // ---- first-pass membership, then importance g_e (R4) summed in
+        // ---- importance g_e (R4) of the first-pass selections, summed in
         //      token order ----
-        for (int i = tid; i < T * k; i += NTHREADS) {
-            const int e = sh.sel_i[i];
-            if (e >= 0 && e < E) atomicOr(&sh.tmask0[e], 1ull << (i / k));
-        }
-        lds_barrier();
         for (int e = tid; e < E; e += NTHREADS) {
             float g = 0.f;
-            const unsigned long long m0 = sh.tmask0[e];
             for (int t = 0; t < T; ++t)
-                if ((m0 >> t) & 1ull)
+                if ((sh.tbits0[t * kTokWords + (e >> 5)] >> (e & 31)) & 1u)
                     for (int j = 0; j < k; ++j)
                         if (sh.sel_i[t * k + j] == e) g += sh.cg[t * k + j];
             sh.g[e] = g;
+            sh.inP[e] = 0;
         }
         lds_barrier();
         // ---- preferred set P*: top-cap by (g desc, index asc) among g > 0 (R5) ----
@@ -314,106 +410,92 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
         // ---- re-select on the biased logits; weights from the original (R6, R7) ----
         for (int t = w; t < T; t += NW) {
             float v[kRouteNJ], vb[kRouteNJ];
-            unsigned key[kRouteNJ];
             load_logits(p.logits + (size_t)t * E, E, v);
             const float lam = sh.lam[t];
 #pragma unroll
             for (int j = 0; j < kRouteNJ; ++j) {
                 const int e = lane + 64 * j;
                 vb[j] = (e < E && sh.inP[e]) ? __fadd_rn(v[j], lam) : v[j];
-                key[j] = float_ord(vb[j]);
             }
-            const unsigned sel = wave_topk_mask<NJ>(key, valid, k);
-            const RankEntry me = wave_rank<NJ>(sel, key, vb, v, k, rbuf);
+            const RankEntry me = wave_select<NJ>(vb, v, valid, k, rbuf, true);
             const bool mine = lane < k;
             const float m = wave_max(mine ? me.v2 : -INFINITY);
             const float ex = mine ? expf(me.v2 - m) : 0.f;
             const float s = wave_sum(ex);
             if (mine) {
+                const float wt = ex / s;
                 sh.fin_i[t * k + lane] = me.idx;
-                sh.fin_w[t * k + lane] = ex / s;
+                sh.fin_w[t * k + lane] = wt;
+                if (write_global) {
+                    p.topk_idx[t * k + lane] = me.idx;
+                    p.topk_w[t * k + lane] = wt;
+                }
             }
+            put_bits(sh.tbits, t, me.idx, k);
         }
         lds_barrier();
     }
 
-    // ---- per-token outputs and membership masks ----
-    for (int i = tid; i < T * k; i += NTHREADS) {
-        const int t = i / k;
-        const int e = sh.fin_i[i];
-        if (write_global) {
-            p.topk_idx[i] = e;
-            p.topk_w[i] = sh.fin_w[i];
+    // ---- union (ascending) and CSR row offsets: wave 0 scans the experts,
+    //      NJ groups of 64; slot = rank in the union ----
+    int *slot_off = reinterpret_cast<int *>(sh.g);  // g is free again: CSR offset per slot
+    if (w == 0) {
+        const unsigned long long below = (1ull << lane) - 1ull;
+        int base_r = 0, base_c = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int e = lane + 64 * j;
+            unsigned long long msk = 0ull;
+            if (e < E)
+                for (int t = 0; t < T; ++t)
+                    msk |= (unsigned long long)((sh.tbits[t * kTokWords + (e >> 5)] >> (e & 31)) & 1u) << t;
+            const int cnt = __popcll(msk);
+            const unsigned long long bal = __ballot(cnt > 0);
+            const int incl = wave_incl_scan(cnt);
+            if (cnt > 0) {
+                const int rank = base_r + __popcll(bal & below);
+                const int off = base_c + incl - cnt;
+                sexp[rank] = e;
+                slot_off[rank] = off;
+                sh.tmask[e] = msk;
+                if (write_global) {
+                    p.union_experts[rank] = e;
+                    p.csr_ptr[rank] = off;
+                    p.slot_expert[rank] = e;
+                }
+            }
+            base_r += __popcll(bal);
+            base_c += __builtin_amdgcn_readlane(incl, 63);
         }
-        if (e >= 0 && e < E) atomicOr(&sh.tmask[e], 1ull << t);
+        if (lane == 0) sh.misc[0] = base_r;
     }
     lds_barrier();
 
-    // ---- union (ascending) via a block scan over experts: rank of each
-    //      union expert and offset of its CSR row ----
-    const int e = tid;
-    const unsigned long long msk = e < E ? sh.tmask[e] : 0ull;
-    const int cnt = __popcll(msk);
-    const int flag = cnt > 0;
-    const unsigned long long bal = __ballot(flag);
-    const int rank_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-    const int incl = wave_incl_scan(cnt);
-    if (lane == 63) {
-        sh.wtot[w] = __popcll(bal);
-        sh.wtot[NW + w] = incl;
-    }
-    lds_barrier();
-    int base_flag = 0, base_cnt = 0, U = 0;
-    for (int q = 0; q < NW; ++q) {
-        if (q < w) {
-            base_flag += sh.wtot[q];
-            base_cnt += sh.wtot[NW + q];
-        }
-        U += sh.wtot[q];
-    }
-    // g (scratch) is reused as the per-expert CSR offset, inP as the rank
-    int *csr_off = reinterpret_cast<int *>(sh.g);
-    if (e < E) {
-        const int rank = base_flag + rank_in_wave;
-        const int off = base_cnt + incl - cnt;
-        csr_off[e] = off;
-        sh.inP[e] = rank;
-        if (flag) {
-            sexp[rank] = e;
+    // ---- slot tables and CSR entries: one thread per (slot, token), each
+    //      entry written once ----
+    const int U = sh.misc[0];
+    for (int i = tid; i < U * T; i += NTHREADS) {
+        const int s = i / T, t = i - s * T;
+        const int e = sexp[s];
+        const unsigned long long msk = sh.tmask[e];
+        float wt = 0.f;
+        int pos = -1;
+        if ((msk >> t) & 1ull) {
+            int jj = 0;
+            for (int j = 0; j < k; ++j)
+                if (sh.fin_i[t * k + j] == e) jj = j;
+            wt = sh.fin_w[t * k + jj];
+            pos = slot_off[s] + __popcll(msk & ((1ull << t) - 1ull));
             if (write_global) {
-                p.union_experts[rank] = e;
-                p.csr_ptr[rank] = off;
-                p.slot_expert[rank] = e;
-            }
-            // tokens of this slot that do not route to it get weight 0
-            for (int t = 0; t < T; ++t) {
-                if (!((msk >> t) & 1ull)) {
-                    tw[rank * T + t] = 0.f;
-                    if (write_global) {
-                        p.tokw[(size_t)rank * T + t] = 0.f;
-                        p.tokpos[(size_t)rank * T + t] = -1;
-                    }
-                }
+                p.csr_tok[pos] = t;
+                p.csr_w[pos] = wt;
+                p.tpos[t * k + jj] = pos;
             }
         }
-    }
-    lds_barrier();
-    // ---- CSR entries: one thread per (token, rank) ----
-    for (int i = tid; i < T * k; i += NTHREADS) {
-        const int t = i / k;
-        const int ex = sh.fin_i[i];
-        if (ex < 0 || ex >= E) continue;
-        const unsigned long long m = sh.tmask[ex];
-        const int pos = csr_off[ex] + __popcll(m & ((1ull << t) - 1ull));
-        const int rank = sh.inP[ex];
-        const float wt = sh.fin_w[i];
-        tw[rank * T + t] = wt;
+        tw[s * T + t] = wt;
         if (write_global) {
-            p.csr_tok[pos] = t;
-            p.csr_w[pos] = wt;
-            p.tpos[i] = pos;
-            p.tokw[(size_t)rank * T + t] = wt;
-            p.tokpos[(size_t)rank * T + t] = pos;
+            p.tokw[(size_t)s * T + t] = wt;
+            p.tokpos[(size_t)s * T + t] = pos;
         }
     }
     if (p.has_shared && tid < T) {

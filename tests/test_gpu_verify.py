@@ -113,6 +113,15 @@ def test_bf16_small_with_bias(T):
     verify_workload(wl, bias_np=(8, 0.5, rng.random(T).astype(np.float32)))
 
 
+@pytest.mark.parametrize("E,k,bias", [(64, 20, False), (64, 16, True), (512, 8, False), (512, 32, True)])
+def test_bf16_wide_routing(E, k, bias):
+    """Selections past 16 ranks (radix search) and 8 entries per lane (E = 512)."""
+    log(f"case bf16 routing E={E} k={k} bias={bias}")
+    wl = small("qwen3_bf16", H=256, I=128, E=E, k=k, T=5, rate=0.05, cid=13)
+    bias_np = (2 * k, 0.5, np.random.default_rng(E + k).random(5).astype(np.float32)) if bias else None
+    verify_workload(wl, bias_np=bias_np)
+
+
 @pytest.mark.parametrize("T,shared", [(5, True), (5, False), (12, True), (40, True)])
 def test_fp8_small(T, shared):
     log(f"case fp8 small T={T} shared={shared}")
