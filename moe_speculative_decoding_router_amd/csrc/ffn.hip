@@ -232,6 +232,7 @@ struct UnitCfg {
 // the weights.  TWL: token weights staged in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kGuWaves = 8;
+constexpr int kGuDynDepth = 3;  // items per workgroup left to the ticket counter
 
 template <int WT, int NT, bool SPLIT, bool FUSED, bool BLDS>
 __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
@@ -242,6 +243,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     __shared__ f32x4 red[2][kGuWaves][NT][64];
     __shared__ int sexp[kMaxExperts + 1];
     __shared__ int nslots_sh;
+    __shared__ int sitem[4];  // items of the tail, ring by item order
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = lane >> 4, lr = lane & 15;
     const int T = p.T, H = p.H, I = p.I, E = p.E, cstride = p.cstride, cols = p.cols;
@@ -300,8 +302,26 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     const int nunits = WT == 1 ? nkt / 2 : nkt;
     const int nbi = (nunits + KU - 1) / KU;                 // batches per item
     const int nb = (nbi + kGuWaves - 1) / kGuWaves;         // per wave per item
-    const int my_items = (items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int F = my_items * nb;
+    // Items: workgroup b takes items b, b + G, ... up to its S0-th; when the
+    // operand is read from L2 (not held in LDS), the workgroups' streaming
+    // rates vary with L2 contention, and the remaining R items are handed
+    // out in order by a device-scope ticket counter, so the workgroups that
+    // stream faster take more of the tail.  A ticket is claimed three items
+    // ahead of its use (right after the barrier of an item) and published to
+    // LDS just before the barrier of the next item, which waits for every
+    // outstanding load anyway.
+    const int G = gridDim.x, bid = blockIdx.x;
+    const bool dyn = !BLDS && p.gu_ticket != nullptr && items >= (kGuDynDepth + 3) * G;
+    const int S0 = dyn ? items / G - kGuDynDepth : 0;
+    const int R = items - S0 * G;
+    auto item_of = [&](int ord) -> int {
+        if (!dyn || ord < S0) {
+            const int it = bid + ord * G;
+            return it < items ? it : -1;
+        }
+        return sitem[ord & 3];
+    };
+    int ticket = 0;  // thread 0: the last claim
     const size_t esz = WT == 1 ? 1 : 2;
     const size_t bstep = (size_t)4 * cstride * 8;                       // global: elements per k-step
     const uint16_t *xb = p.xB + (size_t)g * cstride * 8;                // global: lane group, k-step 0
@@ -317,7 +337,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
         const int ord = f / nb;
         if (ord != c_ord) {
             c_ord = ord;
-            const int item = blockIdx.x + ord * gridDim.x;
+            const int item = item_of(ord);
             const int s = item / rtiles, rt = item - s * rtiles;
             const int e = sexp[s];
             const bool sh = e == E;
@@ -364,13 +384,18 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     // passed the barrier of item i + 1, i.e. after the readers of item i.
     auto finish_item = [&](f32x4 (&acc2)[2][NT], int f) {
         const int ii = f / nb;
-        const int item = blockIdx.x + ii * gridDim.x;
+        const int item = item_of(ii);
         const int s = item / rtiles, rt = item - s * rtiles;
         const int buf = ii & 1;
         fold_acc<NT>(acc2);
 #pragma unroll
         for (int n = 0; n < NT; ++n) red[buf][w][n][lane] = acc2[0][n];
+        // the ticket of item ii + 2, claimed one item ago (ticket t is item
+        // S0 G + t; t >= R: none left)
+        if (dyn && threadIdx.x == 0 && ii + 2 >= S0) sitem[(ii + 2) & 3] = ticket < R ? S0 * G + ticket : -1;
         __syncthreads();
+        if (dyn && threadIdx.x == 0 && ii + 3 >= S0)
+            ticket = __hip_atomic_fetch_add(p.gu_ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int nthr = kGuWaves * 64;
         const int o = ((int)threadIdx.x - (ii % kGuWaves) * 64 + nthr) % nthr;  // rotating owner wave
         if (o < 8 * T) {
@@ -406,16 +431,30 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     for (int n = 0; n < NT; ++n) acc[0][n] = acc[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     // Two register buffers; the prefetch is issued unconditionally (clamped
     // to the last batch) so the number of loads in flight is static.
+    // A batch past the last item re-loads the previous batch and is not
+    // computed, so every wave issues the same loads per step.
+    int vo = 0;  // item order whose validity is cached (order 0 is valid here)
+    bool vv = true;
+    auto valid_ord = [&](int ord) {
+        if (ord != vo) {
+            vo = ord;
+            vv = item_of(ord) >= 0;
+        }
+        return vv;
+    };
     B b0, b1;
     load_batch(b0, 0);
-    for (int f = 0; f < F; f += 2) {
-        load_batch(b1, min(f + 1, F - 1));
+    for (int f = 0;; f += 2) {
+        const bool v1 = valid_ord((f + 1) / nb);
+        load_batch(b1, v1 ? f + 1 : f);
         compute_batch<WT, NT, KU>(b0, acc, true);
         if (f % nb == nb - 1) finish_item(acc, f);
-        load_batch(b0, min(f + 2, F - 1));
-        const bool v1 = f + 1 < F;
-        compute_batch<WT, NT, KU>(b1, acc, v1);
-        if (v1 && (f + 1) % nb == nb - 1) finish_item(acc, f + 1);
+        if (!v1) break;
+        const bool v2 = valid_ord((f + 2) / nb);
+        load_batch(b0, v2 ? f + 2 : f + 1);
+        compute_batch<WT, NT, KU>(b1, acc, true);
+        if ((f + 1) % nb == nb - 1) finish_item(acc, f + 1);
+        if (!v2) break;
     }
 }
 

@@ -46,6 +46,7 @@ struct VerifyParams {
     float *ydown;      // [(T * k + T) * H] per-(token, expert) outputs (float32 weights)
     float *ypart;      // [kDownMaxGrid * 2 * kDownMaxRowTiles * T * 16] down: partial row groups (bf16 / fp8)
     int *tile_cnt;     // [H / 16] down: pieces finished per row group (zeroed by the router kernel)
+    int *gu_ticket;    // [1] gate-up: tail items handed out so far (zeroed by the router kernel)
 };
 
 constexpr int kWaveSize = 64;

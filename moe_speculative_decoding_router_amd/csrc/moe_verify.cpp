@@ -207,6 +207,7 @@ int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const mo
     p.ydown = L.wdtype == MOE_F32 ? reinterpret_cast<float *>(w + lay.ydown) : nullptr;
     p.ypart = L.wdtype == MOE_F32 ? nullptr : reinterpret_cast<float *>(w + lay.ypart);
     p.tile_cnt = L.wdtype == MOE_F32 ? nullptr : reinterpret_cast<int *>(w + lay.tile_cnt);
+    p.gu_ticket = L.wdtype == MOE_F32 ? nullptr : p.tile_cnt + L.H / 16;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int ncu = cu_count();

@@ -37,6 +37,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) 
     if (conv && gid < total) xc = p.x[gid];
     if (p.tile_cnt)  // per-row-tile piece counters of the down kernel
         for (int i = gid; i < p.H / 16; i += gstride) p.tile_cnt[i] = 0;
+    if (p.gu_ticket && gid == 0) p.gu_ticket[0] = 0;
 
     if (e < p.E) {
         const int n = VEC4 ? H / 4 : H;
