@@ -108,7 +108,10 @@ typedef struct {
  *           on `stream` (the kernel is launched with hipExtLaunchKernelGGL);
  *           a stage that runs no kernel in this call (the route stage when
  *           the gate-up kernel routes, the combine stage for bf16/fp8)
- *           records both at that point of the stream. */
+ *           records both at that point of the stream.  When the gate-up
+ *           contraction is split over workgroups (the activation operand
+ *           too large for one compute unit's LDS), the gate-up stage spans
+ *           the gate-up kernel and the SwiGLU combine that follows it. */
 typedef struct {
     float *logits;
     int32_t *topk_idx;

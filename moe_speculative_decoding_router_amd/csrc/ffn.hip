@@ -233,8 +233,13 @@ struct UnitCfg {
 // ---------------------------------------------------------------------------
 constexpr int kGuWaves = 8;
 constexpr int kGuDynDepth = 3;  // items per workgroup left to the ticket counter
+constexpr int kGuMaxSplit = 4;  // most workgroups sharing one item's contraction
 
-template <int WT, int NT, bool SPLIT, bool FUSED, bool BLDS>
+// KS > 1: the contraction of every item is split over KS workgroups;
+// workgroup b takes part b % KS of it and holds only that part's slice of
+// the operand in LDS, and its partial gate and up sums go to gu_part for the
+// SwiGLU combine.
+template <int WT, int NT, bool SPLIT, bool FUSED, bool BLDS, int KS>
 __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     using C = UnitCfg<WT, NT>;
     constexpr int KU = C::KU;
@@ -249,11 +254,16 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     const int T = p.T, H = p.H, I = p.I, E = p.E, cstride = p.cstride, cols = p.cols;
     const int nkt = H / C::KT;
     const int rtiles = I / 8;
+    const int nunits = WT == 1 ? nkt / 2 : nkt;  // contraction units (1 KB per row tile each for bf16)
+    const int hk = KS > 1 ? (int)blockIdx.x % KS : 0;
+    const int nuh = nunits / KS;                  // units of one part (the host checks that KS divides)
+    const int u0 = hk * nuh;                      // first unit of this workgroup's part
+    constexpr int kspu = WT == 1 ? 4 : 1;         // k-steps of 32 per unit
     // dynamic LDS, in order: the activation operand (BLDS), the routing
     // scratch and the token weights (FUSED).  With gu_async_x the operand
     // has a region of its own and its loads fly while the routing runs;
     // otherwise the routing scratch overlays the operand region, filled after.
-    const int ksteps = H / 32;
+    const int ksteps = nuh * kspu;                // k-steps of the part
     const int nx = BLDS ? ksteps * 4 * cols : 0;  // 16-byte operand chunks
     const size_t xb_bytes = (size_t)nx * 16;
     const size_t scr_bytes = FUSED ? (RouteScratch::bytes(T, p.k, E, kGuWaves) + 15) & ~(size_t)15 : 0;
@@ -265,10 +275,11 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     // Direct global -> LDS copy of the operand (one contiguous block, as the
     // column stride equals the column count) by waves w0 .. w0 + nws - 1;
     // lane l of a wave fills chunk i0 + l.
+    const uint16_t *xpart = p.xB + (size_t)u0 * kspu * 4 * cols * 8;  // the part's slice
     auto stage_x = [&](int w0, int nws) {
         if (w < w0) return;
         for (int i0 = (w - w0) * 64; i0 < nx; i0 += nws * 64)
-            if (i0 + lane < nx) load_lds16(p.xB + (size_t)(i0 + lane) * 8, xs + i0);
+            if (i0 + lane < nx) load_lds16(xpart + (size_t)(i0 + lane) * 8, xs + i0);
     };
 
     int nslots;
@@ -293,16 +304,16 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     wait_vm_all();
     __syncthreads();
     const int items = nslots * rtiles;
-    if ((int)blockIdx.x >= items) return;
+    if ((int)blockIdx.x / KS >= min(items, (int)gridDim.x / KS)) return;
 
     // Batches of KU consecutive units; batch b of an item belongs to wave
     // b % kGuWaves, so the workgroup reads one contiguous window that moves
     // through the item.  Every wave runs the same number of batches per item
     // (trailing ones empty), so the reduction barriers line up.
-    const int nunits = WT == 1 ? nkt / 2 : nkt;
-    const int nbi = (nunits + KU - 1) / KU;                 // batches per item
+    const int nbi = (nuh + KU - 1) / KU;                    // batches per item
     const int nb = (nbi + kGuWaves - 1) / kGuWaves;         // per wave per item
-    // Items: workgroup b takes items b, b + G, ... up to its S0-th; when the
+    // Items: workgroup b takes items b, b + G, ... up to its S0-th (G and b
+    // counted among the workgroups of its contraction part).  When the
     // operand is read from L2 (not held in LDS), the workgroups' streaming
     // rates vary with L2 contention, and the remaining R items are handed
     // out in order by a device-scope ticket counter, so the workgroups that
@@ -310,8 +321,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     // ahead of its use (right after the barrier of an item) and published to
     // LDS just before the barrier of the next item, which waits for every
     // outstanding load anyway.
-    const int G = gridDim.x, bid = blockIdx.x;
-    const bool dyn = !BLDS && p.gu_ticket != nullptr && items >= (kGuDynDepth + 3) * G;
+    const int G = gridDim.x / KS, bid = blockIdx.x / KS;
+    const bool dyn = KS == 1 && !BLDS && p.gu_ticket != nullptr && items >= (kGuDynDepth + 3) * G;
     const int S0 = dyn ? items / G - kGuDynDepth : 0;
     const int R = items - S0 * G;
     auto item_of = [&](int ord) -> int {
@@ -355,9 +366,10 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
         const int k0 = ((f % nb) * kGuWaves + w) * KU;
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
-            const int kk = k0 + u;
-            const bool on = kk < nunits;
-            const int kc = on ? kk : nunits - 1;
+            const int kk = k0 + u;                 // unit within the part
+            const bool on = kk < nuh;
+            const int kr = on ? kk : nuh - 1;
+            const int kc = u0 + kr;                // unit within the item
             bt.on[u] = on;
 #pragma unroll
             for (int h = 0; h < B::NA; ++h) bt.a[u][h] = ld_nt(tiles + (size_t)kc * C::USTEP + h * 1024);
@@ -367,7 +379,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
                     if (BLDS)
-                        bt.b[u][q][n] = xs[(ks * 4 + g) * cols + (coff[n] >> 3)];
+                        bt.b[u][q][n] = xs[((kr * B::NS + q) * 4 + g) * cols + (coff[n] >> 3)];
                     else
                         bt.b[u][q][n] = *reinterpret_cast<const u32x4 *>(xb + (size_t)ks * bstep + coff[n]);
                 }
@@ -414,13 +426,20 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
                     uv += red[buf][q][n][lu][j];
                 }
             }
-            const float wt = FUSED ? tw_lds[s * T + t] : p.tokw[(size_t)s * T + t];
-            const float hv = wt * (silu(gv) * uv);
-            const uint16_t hi = f32_to_bf16_rne(hv);
-            uint16_t *hb = p.hB + (size_t)s * I * cstride;
             const int il = 8 * rt + r;
-            hb[b_index(il, t, cstride, WT == 1)] = hi;
-            if (SPLIT) hb[b_index(il, T + t, cstride, WT == 1)] = f32_to_bf16_rne(hv - bf16_to_f32(hi));
+            if (KS > 1) {
+                // this part's sums; the SwiGLU combine adds the parts
+                float *pp = p.gu_part + (((size_t)hk * p.max_slots + s) * I + il) * 2 * T;
+                pp[t] = gv;
+                pp[T + t] = uv;
+            } else {
+                const float wt = FUSED ? tw_lds[s * T + t] : p.tokw[(size_t)s * T + t];
+                const float hv = wt * (silu(gv) * uv);
+                const uint16_t hi = f32_to_bf16_rne(hv);
+                uint16_t *hb = p.hB + (size_t)s * I * cstride;
+                hb[b_index(il, t, cstride, WT == 1)] = hi;
+                if (SPLIT) hb[b_index(il, T + t, cstride, WT == 1)] = f32_to_bf16_rne(hv - bf16_to_f32(hi));
+            }
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc2[0][n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -740,6 +759,35 @@ __global__ __launch_bounds__(kDnWaves * 64) void down_kernel(VerifyParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// SwiGLU of a split contraction: h = w_t * SiLU(sum of the gate parts) *
+// (sum of the up parts), parts added in part order, written as the bf16
+// operand of the down kernel.  One thread per (slot, intermediate row,
+// token); consecutive threads read consecutive tokens.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void swiglu_kernel(VerifyParams p, int ks) {
+    const int T = p.T, I = p.I, cstride = p.cstride;
+    const bool fp8 = p.wdtype == 2;
+    const int nslots = min(p.meta[1], p.max_slots);
+    const long long total = (long long)nslots * I * T;
+    for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
+        const int t = (int)(idx % T);
+        const long long r = idx / T;
+        const int il = (int)(r % I), s = (int)(r / I);
+        float gv = 0.f, uv = 0.f;
+        for (int h = 0; h < ks; ++h) {
+            const float *pp = p.gu_part + (((size_t)h * p.max_slots + s) * I + il) * 2 * T;
+            gv += pp[t];
+            uv += pp[T + t];
+        }
+        const float hv = p.tokw[(size_t)s * T + t] * (silu(gv) * uv);
+        const uint16_t hi = f32_to_bf16_rne(hv);
+        uint16_t *hb = p.hB + (size_t)s * I * cstride;
+        hb[b_index(il, t, cstride, fp8)] = hi;
+        if (p.split) hb[b_index(il, T + t, cstride, fp8)] = f32_to_bf16_rne(hv - bf16_to_f32(hi));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Float32 weights: one wave per (slot, row), lanes over the contraction.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kFfnThreads) void gateup_f32_kernel(VerifyParams p) {
@@ -832,23 +880,30 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyParams p) {
 
 // LDS plan of the gate-up kernel: routing fused into its prologue and the
 // activation operand held in LDS when they fit in one compute unit.
+// ks: workgroups that share the contraction of an item (the operand slice
+// of each must fit in LDS); the smallest that fits is taken.
 struct GuPlan {
     bool fused, blds, async_x;
+    int ks;
     size_t dyn;
 };
 
 GuPlan plan_gateup(const VerifyParams &p) {
     const int nt = (p.cols + 15) / 16;
-    const size_t stat = sizeof(float) * 4 * 2 * kGuWaves * nt * 64 + sizeof(int) * (kMaxExperts + 2);
+    const size_t stat = sizeof(float) * 4 * 2 * kGuWaves * nt * 64 + sizeof(int) * (kMaxExperts + 6);
     auto al = [](size_t v) { return (v + 15) & ~(size_t)15; };
     const size_t scr = al(RouteScratch::bytes(p.T, p.k, p.E, kGuWaves));
     const size_t tw = (size_t)p.max_slots * p.T * sizeof(float);
-    const size_t xb = (size_t)(p.H / 32) * 4 * p.cols * 16;
-    const size_t over = xb > scr ? xb : scr;
-    if (xb + scr + tw + stat <= kLdsPerCu) return {true, true, true, xb + scr + tw};
-    if (over + tw + stat <= kLdsPerCu) return {true, true, false, over + tw};
-    if (scr + tw + stat <= kLdsPerCu) return {true, false, false, scr + tw};
-    return {false, false, false, 0};
+    const int nunits = p.wdtype == 2 ? p.H / 128 : p.H / 32;
+    for (int ks = 1; ks <= kGuMaxSplit; ks *= 2) {
+        if (nunits % ks != 0) break;
+        const size_t xb = (size_t)(p.H / 32 / ks) * 4 * p.cols * 16;
+        const size_t over = xb > scr ? xb : scr;
+        if (xb + scr + tw + stat <= kLdsPerCu) return {true, true, true, ks, xb + scr + tw};
+        if (over + tw + stat <= kLdsPerCu) return {true, true, false, ks, over + tw};
+    }
+    if (scr + tw + stat <= kLdsPerCu) return {true, false, false, 1, scr + tw};
+    return {false, false, false, 1, 0};
 }
 
 template <typename K>
@@ -866,9 +921,13 @@ hipError_t launch_one(const VerifyParams &p, int n_cu, hipStream_t s, KernelEven
         const GuPlan pl = plan_gateup(p);
         VerifyParams q = p;
         q.gu_async_x = pl.async_x ? 1 : 0;
-        if (pl.fused && pl.blds) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true>, q, pl.dyn, n_cu, s, ev);
-        if (pl.fused) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, false>, q, pl.dyn, n_cu, s, ev);
-        return launch_gu(gateup_kernel<WT, NT, SPLIT, false, false>, q, 0, n_cu, s, ev);
+        if (pl.fused && pl.blds) {
+            if (pl.ks == 1) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 1>, q, pl.dyn, n_cu, s, ev);
+            if (pl.ks == 2) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 2>, q, pl.dyn, n_cu, s, ev);
+            return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 4>, q, pl.dyn, n_cu, s, ev);
+        }
+        if (pl.fused) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, false, 1>, q, pl.dyn, n_cu, s, ev);
+        return launch_gu(gateup_kernel<WT, NT, SPLIT, false, false, 1>, q, 0, n_cu, s, ev);
     } else {
         // one workgroup per compute unit; the work splits evenly over them
         const int grid = n_cu < kDownMaxGrid ? n_cu : kDownMaxGrid;
@@ -898,6 +957,14 @@ hipError_t launch_mfma(const VerifyParams &p, int n_cu, hipStream_t s, KernelEve
 }  // namespace
 
 bool gateup_fuses_routing(const VerifyParams &p) { return p.wdtype != 0 && plan_gateup(p).fused; }
+
+int gateup_ksplit(const VerifyParams &p) { return p.wdtype != 0 ? plan_gateup(p).ks : 1; }
+
+hipError_t launch_swiglu(const VerifyParams &p, int ks, hipStream_t s, KernelEvents ev) {
+    long long blocks = ((long long)p.max_slots * p.I * p.T + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    return launch_k(swiglu_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ev, p, ks);
+}
 
 hipError_t launch_gateup(const VerifyParams &p, int n_cu, hipStream_t s, KernelEvents ev) {
     const int grid = n_cu * 4;

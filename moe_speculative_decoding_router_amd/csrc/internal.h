@@ -47,21 +47,23 @@ struct VerifyParams {
     float *ypart;      // [kDownMaxGrid * 2 * kDownMaxRowTiles * T * 16] down: partial row groups (bf16 / fp8)
     int *tile_cnt;     // [H / 16] down: pieces finished per row group (zeroed by the router kernel)
     int *gu_ticket;    // [1] gate-up: tail items handed out so far (zeroed by the router kernel)
+    float *gu_part;    // [ks][max_slots][I][2][T] gate-up: partial gate and up sums of a split contraction
 };
 
 constexpr int kWaveSize = 64;
 
 // Launchers (enqueue only; return hipError_t of the launch).
-// Optional timing of one launch: with both events set, the kernel is
-// launched through hipExtLaunchKernelGGL so that the events mark the start
-// and the end of its execution on the stream.
+// Optional timing of one launch: with an event set, the kernel is launched
+// through hipExtLaunchKernelGGL so that the events mark the start and the
+// end of its execution on the stream (either may be null, so a stage can
+// span two launches).
 struct KernelEvents {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 
 template <typename F, typename... Args>
 hipError_t launch_k(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, KernelEvents ev, Args... args) {
-    if (ev.start && ev.stop)
+    if (ev.start || ev.stop)
         hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
     else
         hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
@@ -72,6 +74,10 @@ hipError_t launch_router(const VerifyParams &p, hipStream_t s, KernelEvents ev =
 hipError_t launch_route(const VerifyParams &p, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_gateup(const VerifyParams &p, int n_cu, hipStream_t s, KernelEvents ev = {});
 bool gateup_fuses_routing(const VerifyParams &p);  // routing runs in the gate-up prologue
+// Workgroups sharing the contraction of one gate-up item (1: none); with
+// more than one, launch_swiglu finishes the hidden activations.
+int gateup_ksplit(const VerifyParams &p);
+hipError_t launch_swiglu(const VerifyParams &p, int ks, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_down(const VerifyParams &p, int n_cu, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_combine(const VerifyParams &p, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_pack(const void *src, void *dst, int E, int R, int K, int esz, int interleave, int half,

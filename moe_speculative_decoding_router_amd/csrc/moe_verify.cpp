@@ -42,7 +42,8 @@ int cu_count() {
 
 struct Layout {
     size_t logits, topk_idx, topk_w, meta, union_experts, csr_ptr, csr_tok, csr_w, pstar;
-    size_t slot_expert, tokw, tokpos, tpos, xB, hB, h32, ydown, ypart, tile_cnt, total;
+    size_t slot_expert, tokw, tokpos, tpos, xB, hB, h32, ydown, ypart, tile_cnt, gu_part, total;
+    int ks;  // workgroups sharing one gate-up item's contraction
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -53,8 +54,26 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // tile at one tile per 16 tokens.
 bool split_mode(int T) { return 2 * T <= 16; }
 
+// The planning fields of the kernel parameters (what the gate-up plan reads).
+moe::VerifyParams plan_params(const moe_layer &L, int T) {
+    moe::VerifyParams p{};
+    p.T = T;
+    p.H = L.H;
+    p.I = L.I;
+    p.E = L.E;
+    p.k = L.k;
+    p.wdtype = L.wdtype;
+    p.split = split_mode(T) ? 1 : 0;
+    p.cols = p.split ? 2 * T : T;
+    p.cstride = p.cols;
+    p.has_shared = L.Wsh_gu != nullptr;
+    p.max_slots = std::min(L.E, T * L.k) + p.has_shared;
+    return p;
+}
+
 Layout make_layout(const moe_layer &L, int T) {
     Layout o{};
+    o.ks = moe::gateup_ksplit(plan_params(L, T));
     const size_t E = L.E, k = L.k, H = L.H, I = L.I;
     const size_t slots = (size_t)std::min<long>(L.E, (long)T * L.k) + 1;
     const size_t cols = split_mode(T) ? 2 * T : T;
@@ -79,7 +98,7 @@ Layout make_layout(const moe_layer &L, int T) {
     o.tokpos = take(slots * T * 4);
     o.tpos = take(T * k * 4);
     if (L.wdtype == MOE_F32) {
-        o.xB = o.hB = o.ypart = o.tile_cnt = 0;
+        o.xB = o.hB = o.ypart = o.tile_cnt = o.gu_part = 0;
         o.h32 = take(slots * T * I * 4);
         o.ydown = take(((size_t)T * k + T) * H * 4);
     } else {
@@ -88,6 +107,7 @@ Layout make_layout(const moe_layer &L, int T) {
         o.h32 = o.ydown = 0;
         o.ypart = take((size_t)moe::kDownMaxGrid * 2 * moe::kDownMaxRowTiles * T * 16 * 4);
         o.tile_cnt = take((H / 16 + 1) * 4);
+        o.gu_part = o.ks > 1 ? take((size_t)o.ks * slots * I * 2 * T * 4) : 0;
     }
     o.total = off;
     return o;
@@ -153,18 +173,7 @@ int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const mo
         return fail(MOE_EINVAL, "x and y must be 16-byte aligned");
 
     char *w = static_cast<char *>(ws);
-    moe::VerifyParams p{};
-    p.T = T;
-    p.H = L.H;
-    p.I = L.I;
-    p.E = L.E;
-    p.k = L.k;
-    p.wdtype = L.wdtype;
-    p.split = split_mode(T) ? 1 : 0;
-    p.cols = p.split ? 2 * T : T;
-    p.cstride = p.cols;
-    p.has_shared = L.Wsh_gu != nullptr;
-    p.max_slots = std::min(L.E, T * L.k) + p.has_shared;
+    moe::VerifyParams p = plan_params(L, T);
     p.bias_on = bias != nullptr;
     p.cap = bias ? bias->cap : 0;
     p.alpha = bias ? bias->alpha : 0.f;
@@ -208,6 +217,7 @@ int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const mo
     p.ypart = L.wdtype == MOE_F32 ? nullptr : reinterpret_cast<float *>(w + lay.ypart);
     p.tile_cnt = L.wdtype == MOE_F32 ? nullptr : reinterpret_cast<int *>(w + lay.tile_cnt);
     p.gu_ticket = L.wdtype == MOE_F32 ? nullptr : p.tile_cnt + L.H / 16;
+    p.gu_part = lay.ks > 1 ? reinterpret_cast<float *>(w + lay.gu_part) : nullptr;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int ncu = cu_count();
@@ -228,7 +238,14 @@ int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const mo
     } else if (!no_kernel(1)) {
         return fail(MOE_EHIP, "hipEventRecord failed");
     }
-    if ((err = moe::launch_gateup(p, ncu, s, kev[2])) != hipSuccess) goto hip_fail;
+    if (lay.ks == 1) {
+        if ((err = moe::launch_gateup(p, ncu, s, kev[2])) != hipSuccess) goto hip_fail;
+    } else {
+        // a split gate-up contraction is finished by the SwiGLU combine; the
+        // gate-up stage's events span both launches
+        if ((err = moe::launch_gateup(p, ncu, s, {kev[2].start, nullptr})) != hipSuccess) goto hip_fail;
+        if ((err = moe::launch_swiglu(p, lay.ks, s, {nullptr, kev[2].stop})) != hipSuccess) goto hip_fail;
+    }
     if ((err = moe::launch_down(p, ncu, s, kev[3])) != hipSuccess) goto hip_fail;
     if (L.wdtype == MOE_F32) {
         if ((err = moe::launch_combine(p, s, kev[4])) != hipSuccess) goto hip_fail;

@@ -129,6 +129,27 @@ def test_fp8_small(T, shared):
     verify_workload(wl)
 
 
+@pytest.mark.parametrize("T", [20, 32, 64])
+def test_bf16_wide_operand(T):
+    """H = 4096 with 20, 32 and 64 token columns: the activation operand does
+    not fit in LDS whole, so the contraction of each item is split over 2
+    (T = 20) or 4 (T = 32) workgroups and finished by the SwiGLU combine; at
+    T = 64 no slice fits and the operand is read from L2 with the tail items
+    handed out by tickets (I = 1024 gives the 16 experts enough items)."""
+    I = 1024 if T == 64 else 256
+    log(f"case bf16 H=4096 I={I} T={T}")
+    wl = small("qwen3_bf16", H=4096, I=I, E=16, k=4, T=T, rate=0.05, cid=14)
+    verify_workload(wl)
+
+
+def test_fp8_split_contraction():
+    """fp8 with 40 token columns at H = 2048: contraction split over 2
+    workgroups (per-block scales applied per part)."""
+    log("case fp8 H=2048 T=40")
+    wl = small("deepseek_fp8", H=2048, I=256, E=16, k=4, T=40, shared=True, cid=15)
+    verify_workload(wl)
+
+
 def test_bf16_gptoss_contraction_tail():
     log("case bf16 H=I=2880 (90 k-steps, uneven split), E=16")
     wl = small("gptoss_bf16", E=16, cid=12)
