@@ -176,6 +176,13 @@ def main() -> int:
     }
     ffn_ms = stage_ms[:, 2] + stage_ms[:, 3]
     ffn_bytes = kbytes["gate_up"] + kbytes["down"]
+    # router + gate-up + down of one verify call (the stages that run kernels
+    # for matrix-core weights; a stage without a kernel records its events
+    # back to back, which reads a few microseconds)
+    call_us = (stage_ms[:, 0] + stage_ms[:, 2] + stage_ms[:, 3]) * 1e3
+
+    out_extra = {"read_stream": read_stream(m, torch, dev),
+                 "select_4096_trees": select_timing(m, synth, wl, dev, stream, nt=4096)}
 
     # ---------------- CPU oracle baseline (bounded sample) ----------------
     cpu = None
@@ -203,6 +210,7 @@ def main() -> int:
         "unique_expert_MB_per_layer": round(float(np.mean(bytes_layer)) / 1e6, 1),
         "us_per_step": round(ms_step * 1e3, 2),
         "verify_us_per_layer_incl_select": round(ms_step * 1e3 / ML, 2),
+        "verify_kernel_us_per_layer_p10_p50_p90": [round(float(v), 2) for v in np.percentile(call_us, [10, 50, 90])],
     }
     # the kernels every bf16/fp8 call runs (the route stage runs a kernel only
     # when the routing scratch exceeds LDS; combine only for float32 weights)
@@ -214,6 +222,7 @@ def main() -> int:
                          "bytes_per_launch": round(float(kbytes[name].mean())),
                          "GBs": round(float(kbytes[name].sum() / (stage_ms[:, q].sum() * 1e-3) / 1e9), 1)}
     out["kernels"] = kernels
+    out.update(out_extra)
     # Cost model of the expansion step ([S2-MoE] component 1, Fig. 6): verify
     # latency = a + T_exp * (unique experts).  Least-squares fit over the
     # sampled calls (router + gate-up + down kernel time against U).
@@ -337,6 +346,66 @@ def measured_traffic(workload, kernel):
     return int(float(v)) if v else None
 
 
+def read_stream(m, torch, dev, gib=4, reps=10):
+    """Context for the roofline: the streaming ceiling measured with the
+    library's read probe (moe_stream_read: the FFN kernels' load pattern, one
+    workgroup of 8 waves per compute unit, every byte folded into a
+    checksum) over `gib` GiB, best of `reps` launches."""
+    t = torch.ones((gib << 30) // 4, dtype=torch.int32, device=dev)
+    chk = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        m.stream_read(t, chk)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        m.stream_read(t, chk)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None or ms < best else best
+    del t
+    gbs = (gib << 30) / (best * 1e-3) / 1e9
+    err(f"[bench] read stream (moe_stream_read, {gib} GiB): {gbs:.0f} GB/s")
+    return {"GBs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "kernel": f"read_probe_kernel (moe_stream_read) over {gib} GiB, best of {reps}"}
+
+
+def select_timing(m, synth, wl, dev, stream, nt=4096, reps=20):
+    """select_drafts on a batch of nt draft trees of this workload's shape
+    (depth 3, top-2: 14 nodes; footprints over the model's MoE layers), gamma
+    4; one launch for the batch.  Reported with the bytes of P and the
+    footprints, which the kernel reads once."""
+    import numpy as np
+    import torch
+    # 256 distinct trees tiled to nt (the kernel's work does not depend on
+    # the trees being distinct; generating 4096 takes about a minute)
+    base = min(nt, 256)
+    trees = synth.draft_trees(seed=5, nt=base, n_layers=MODEL_LAYERS[wl.name], E=wl.E, k=wl.k)
+    reps_t = (nt + base - 1) // base
+    P = np.ascontiguousarray(np.tile(trees.P, (reps_t, 1))[:nt])
+    F = np.ascontiguousarray(np.tile(trees.F, (reps_t, 1, 1))[:nt])
+    P_d = torch.from_numpy(P).to(dev)
+    F_d = torch.from_numpy(F.view(np.int32)).to(dev)
+    S_d = torch.empty((nt, 4), dtype=torch.int32, device=dev)
+    for _ in range(3):
+        m.select_drafts(trees.parent, P_d, F_d, 4, out=S_d)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        m.select_drafts(trees.parent, P_d, F_d, 4, out=S_d)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    nbytes = F.nbytes + P.nbytes
+    err(f"[bench] select_drafts, {nt} trees: {us:.1f} us per launch, {nbytes / (us * 1e-6) / 1e9:.0f} GB/s")
+    return {"trees": nt, "distinct_trees": base, "nodes_per_tree": int(P.shape[1]), "words_per_footprint": int(F.shape[2]),
+            "us_per_launch": round(us, 2), "bytes_read": int(nbytes),
+            "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def cpu_baseline(wl, budget_s, U0, be, n_sh):
     """The CPU oracle (plain NumPy, float64) on layer 0 of the same workload:
     router logits, routing, and the per-token dense loop over each token's
@@ -376,10 +445,34 @@ def cpu_baseline(wl, budget_s, U0, be, n_sh):
     U = len(omoe.expert_union(r.topk_idx))
     gbs = (U + n_sh) * be / per_layer / 1e9
     err(f"[bench] cpu oracle: {per_layer * 1e3:.1f} ms/layer ({reps} reps), {gbs:.2f} GB/s, {threads} threads")
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"layer 0 of {wl.name} (union {U} experts), {reps} repetitions of router logits + "
-                      f"routing + per-token dense float64 loop; {per_layer * 1e3:.1f} ms/layer; expert "
-                      f"regeneration and decoding ({t_regen:.1f} s) untimed"}
+    # the same on one thread, one repetition
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t = time.perf_counter()
+            lg = omoe.router_logits(x, Wr).astype(np.float32)
+            rr = omoe.route(lg, wl.k)
+            omoe.moe_layer(x, rr.topk_idx, rr.topk_w, lambda e: cache[e], shared=shared)
+            t1 = time.perf_counter() - t
+        single = {"value": round((U + n_sh) * be / t1 / 1e9, 3), "ms_per_layer": round(t1 * 1e3, 1)}
+        err(f"[bench] cpu oracle, 1 thread: {t1 * 1e3:.1f} ms/layer")
+    except Exception:
+        pass
+    # the selection oracle ([EcoSpec] section 3.3) per batch of 16 trees
+    from oracle import select as osel
+    trees = synth.draft_trees(seed=5, nt=16, n_layers=MODEL_LAYERS[wl.name], E=wl.E, k=wl.k)
+    t = time.perf_counter()
+    osel.select_drafts_batch(trees.P, trees.F, 4)
+    sel_ms = (time.perf_counter() - t) * 1e3
+    out = {"value": round(gbs, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"layer 0 of {wl.name} (union {U} experts), {reps} repetitions of router logits + "
+                     f"routing + per-token dense float64 loop; {per_layer * 1e3:.1f} ms/layer; expert "
+                     f"regeneration and decoding ({t_regen:.1f} s) untimed",
+           "select_ms_per_16_trees": round(sel_ms, 2)}
+    if single is not None:
+        out["single_thread"] = single
+    return out
 
 
 if __name__ == "__main__":

@@ -145,6 +145,16 @@ typedef struct {
 int moe_pack_weights(const void *src, void *dst, int32_t E, int32_t rows, int32_t K, int32_t wdtype,
                      int32_t gate_up, void *stream);
 
+/* Streaming-read probe (a measurement aid, not part of the verify path):
+ * reads `bytes` of device memory at src with the FFN kernels' load pattern
+ * (16-byte non-temporal loads, 1 KB contiguous per wave and load, one
+ * workgroup of 8 waves per compute unit) and XORs the 32-bit words into
+ * *checksum (device; the caller zeroes it first), so the bytes are used.
+ * Its rate is the achievable streaming ceiling against which the FFN
+ * kernels' HBM rates are read.  bytes: positive multiple of 16; src 16-byte
+ * aligned.  Asynchronous on `stream`. */
+int moe_stream_read(const void *src, size_t bytes, uint32_t *checksum, void *stream);
+
 /* Workspace bytes that moe_verify_layer needs for this layer, T and bias
  * (host computation only; bias may be NULL).  Returns 0 for invalid input. */
 size_t moe_verify_workspace_bytes(const moe_layer *layer, int32_t T, const moe_bias *bias);

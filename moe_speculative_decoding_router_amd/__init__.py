@@ -33,7 +33,7 @@ NUM_STAGES = 5
 STAGE_NAMES = ("router", "route", "gate_up", "down", "combine")
 EXPORTED = ("moe_pack_weights", "moe_verify_workspace_bytes", "moe_verify_layer", "union_stats",
             "select_drafts", "select_drafts_static", "expand_drafts", "union_stats_segments", "gate_depths",
-            "moe_last_error")
+            "moe_stream_read", "moe_last_error")
 
 _vp, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.gate_depths.restype = ctypes.c_int
         L.moe_pack_weights.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
         L.moe_pack_weights.restype = ctypes.c_int
+        L.moe_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
+        L.moe_stream_read.restype = ctypes.c_int
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -158,6 +160,18 @@ def pack_weights(src, wdtype: str, gate_up: bool, out=None, stream=None):
     s = stream if stream is not None else torch.cuda.current_stream(src.device).cuda_stream
     _check(lib().moe_pack_weights(src.data_ptr(), dst.data_ptr(), E, rows, K, DTYPES[wdtype], int(bool(gate_up)), s))
     return dst
+
+
+def stream_read(src, checksum, stream=None) -> None:
+    """moe_stream_read: stream `src` (a contiguous device tensor, byte size a
+    multiple of 16) with the FFN kernels' load pattern, XOR-folding its
+    32-bit words into `checksum` (a zeroed int32 device tensor of 1)."""
+    import torch
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(src.device).cuda_stream
+    _check(lib().moe_stream_read(src.data_ptr(), nbytes, checksum.data_ptr(), s))
 
 
 def pack_layer_tensors(W: dict, wdtype: str) -> dict:

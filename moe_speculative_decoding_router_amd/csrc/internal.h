@@ -82,6 +82,7 @@ hipError_t launch_down(const VerifyParams &p, int n_cu, hipStream_t s, KernelEve
 hipError_t launch_combine(const VerifyParams &p, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_pack(const void *src, void *dst, int E, int R, int K, int esz, int interleave, int half,
                        hipStream_t s);
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, int n_cu, hipStream_t s);
 hipError_t launch_union_stats(const int32_t *topk_idx, int nL, int T, int k, int E, int32_t *counts,
                               float *reuse, hipStream_t s);
 hipError_t launch_select(int N, const float *P, const uint32_t *F, int W, int gamma, float eps,

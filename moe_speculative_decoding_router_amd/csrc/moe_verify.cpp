@@ -278,6 +278,15 @@ int moe_pack_weights(const void *src, void *dst, int32_t E, int32_t rows, int32_
     return MOE_OK;
 }
 
+int moe_stream_read(const void *src, size_t bytes, uint32_t *checksum, void *stream) {
+    if (!src || !checksum) return fail(MOE_EINVAL, "NULL pointer");
+    if (bytes == 0 || bytes % 16 != 0) return fail(MOE_EINVAL, "bytes must be a positive multiple of 16");
+    if (reinterpret_cast<uintptr_t>(src) & 15) return fail(MOE_EINVAL, "src must be 16-byte aligned");
+    hipError_t err = moe::launch_read_probe(src, bytes, checksum, cu_count(), static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(MOE_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return MOE_OK;
+}
+
 int union_stats(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32_t E, int32_t *counts,
                 float *reuse, void *stream) {
     if (!topk_idx || !counts || !reuse) return fail(MOE_EINVAL, "NULL pointer");

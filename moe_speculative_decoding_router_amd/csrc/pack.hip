@@ -53,7 +53,49 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ s
     }
 }
 
+// ---------------------------------------------------------------------------
+// Read probe: streams n16 16-byte words with the load pattern of the FFN
+// kernels (each wave reads 1 KB of contiguous memory per non-temporal
+// 16-byte load per lane, four loads in flight; one workgroup of 8 waves per
+// compute unit) and folds them into an XOR checksum, so every byte is used.
+// Its rate is the streaming ceiling the FFN kernels are measured against.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld_nt16(const uint8_t *ptr) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ptr));
+}
+
+__global__ __launch_bounds__(512) void read_probe_kernel(const uint8_t *__restrict__ src, long long n16,
+                                                         uint32_t *sink) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const long long nw = (long long)gridDim.x * 8;
+    const long long nchunks = n16 / 64;  // whole 1 KB chunks
+    long long c = (long long)blockIdx.x * 8 + w;
+    u32x4 acc = u32x4{0u, 0u, 0u, 0u};
+    for (; c + 3 * nw < nchunks; c += 4 * nw) {
+        const u32x4 a0 = ld_nt16(src + ((c)*64 + lane) * 16);
+        const u32x4 a1 = ld_nt16(src + ((c + nw) * 64 + lane) * 16);
+        const u32x4 a2 = ld_nt16(src + ((c + 2 * nw) * 64 + lane) * 16);
+        const u32x4 a3 = ld_nt16(src + ((c + 3 * nw) * 64 + lane) * 16);
+        acc ^= (a0 ^ a1) ^ (a2 ^ a3);
+    }
+    for (; c < nchunks; c += nw) acc ^= ld_nt16(src + (c * 64 + lane) * 16);
+    if (blockIdx.x == 0 && w == 0) {  // the words past the last whole chunk
+        const long long i = nchunks * 64 + lane;
+        if (i < n16) acc ^= ld_nt16(src + i * 16);
+    }
+    unsigned x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x ^= (unsigned)__shfl_xor((int)x, o);
+    if (lane == 0) atomicXor(sink, x);
+}
+
 }  // namespace
+
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, int n_cu, hipStream_t s) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(n_cu), dim3(512), 0, s, static_cast<const uint8_t *>(src),
+                       (long long)(bytes / 16), sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack(const void *src, void *dst, int E, int R, int K, int esz, int interleave, int half,
                        hipStream_t s) {

@@ -139,3 +139,16 @@ def test_ragged_validation(lib):
     assert lib.gate_depths(16, 16, 4, 4, 1025, 1.0, 1.0, 16, None) == -1    # W > 1024
     assert lib.gate_depths(16, 16, 4, 4, 8, 0.0, 1.0, 16, None) == -1       # t_base <= 0
     assert lib.gate_depths(None, 16, 4, 4, 8, 1.0, 1.0, 16, None) == -1     # NULL
+
+
+def test_stream_read_validation(lib):
+    """moe_stream_read rejects bad arguments before any device work."""
+    import ctypes
+    buf = (ctypes.c_uint8 * 64)()
+    out = (ctypes.c_uint32 * 1)()
+    addr = (ctypes.addressof(buf) + 15) & ~15
+    assert lib.moe_stream_read(None, 16, ctypes.addressof(out), None) == -1
+    assert lib.moe_stream_read(addr, 16, None, None) == -1
+    assert lib.moe_stream_read(addr, 0, ctypes.addressof(out), None) == -1
+    assert lib.moe_stream_read(addr, 24, ctypes.addressof(out), None) == -1
+    assert lib.moe_stream_read(addr + 4, 16, ctypes.addressof(out), None) == -1

@@ -196,3 +196,18 @@ def test_pack_layout(wdtype, gate_up):
     torch.cuda.synchronize()
     got = out.cpu().numpy().view(np.uint8).ravel()
     assert np.array_equal(got, expected_pack(src, gate_up, 2 if wdtype == "bf16" else 1))
+
+
+@pytest.mark.parametrize("nbytes", [16, 1008, 1040, 5 * 2**20 + 48, 256 * 2**20])
+def test_stream_read_checksum(nbytes):
+    """The read probe touches every byte once: its XOR checksum equals the
+    host's, for sizes below one chunk, ragged tails and several passes."""
+    log(f"case stream_read {nbytes} bytes")
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    src = to_dev(host.view(np.int32))
+    chk = torch.zeros(1, dtype=torch.int32, device=src.device)
+    m.stream_read(src, chk)
+    torch.cuda.synchronize()
+    want = int(np.bitwise_xor.reduce(host)) if host.size else 0
+    assert (int(chk.item()) & 0xFFFFFFFF) == want

@@ -245,3 +245,33 @@ def test_full_qwen3_batch4_layer(bias_on):
         bias = (16, 0.5, rng.random(wl.T).astype(np.float32))
     out, r = verify_workload(wl, bias_np=bias)
     log(f"    union {int(out['union_size'][0])} experts")
+
+
+@pytest.mark.parametrize("part", [0, 1])
+def test_deepseek_fp8_stack(part):
+    """The 16-layer DeepSeek-shaped fp8 stack (256 experts + shared):
+    routing, union and CSR bit for bit against the oracle on every layer,
+    outputs on the first, middle and last layers."""
+    wl = synth.WORKLOADS["deepseek_fp8"]
+    L = wl.n_layers
+    for layer in range(part * L // 2, (part + 1) * L // 2):
+        out_check = layer in (0, L // 2, L - 1)
+        log(f"case deepseek_fp8 stack layer {layer}{' with outputs' if out_check else ''}")
+        verify_workload(wl, layer=layer, check_y=out_check)
+
+
+@pytest.mark.parametrize("bias_on,part", [(False, 0), (False, 1), (True, 0), (True, 1)])
+def test_qwen3_batch4_stack(bias_on, part):
+    """The 40-layer batched Qwen3 stack (4 sequences x 5 tokens), without
+    and with the reuse bias (cap 16, alpha 0.5): routing, union and CSR bit
+    for bit on every layer, outputs on the first, middle and last layers."""
+    wl = synth.WORKLOADS["qwen3_batch4_bf16"]
+    L = wl.n_layers
+    bias = None
+    if bias_on:
+        rng = synth.rng_for(0, wl.cid, 999)
+        bias = (16, 0.5, rng.random(wl.T).astype(np.float32))
+    for layer in range(part * L // 2, (part + 1) * L // 2):
+        out_check = layer in (0, L // 2, L - 1)
+        log(f"case qwen3_batch4 stack layer {layer} bias={bias_on}{' with outputs' if out_check else ''}")
+        verify_workload(wl, layer=layer, bias_np=bias, check_y=out_check)
