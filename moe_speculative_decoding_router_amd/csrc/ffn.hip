@@ -262,44 +262,48 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     // dynamic LDS, in order: the activation operand (BLDS), the routing
     // scratch and the token weights (FUSED).  With gu_async_x the operand
     // has a region of its own and its loads fly while the routing runs;
-    // otherwise the routing scratch overlays the operand region, filled after.
+    // otherwise the routing scratch overlays the end of the operand region:
+    // the chunks below it are loaded while the routing runs, the rest after.
     const int ksteps = nuh * kspu;                // k-steps of the part
     const int nx = BLDS ? ksteps * 4 * cols : 0;  // 16-byte operand chunks
     const size_t xb_bytes = (size_t)nx * 16;
     const size_t scr_bytes = FUSED ? (RouteScratch::bytes(T, p.k, E, kGuWaves) + 15) & ~(size_t)15 : 0;
     const bool async_x = BLDS && p.gu_async_x != 0;
+    // operand chunks that can be loaded before the routing is done
+    const int early = async_x ? nx : (BLDS && xb_bytes >= scr_bytes ? (int)((xb_bytes - scr_bytes) / 16) : 0);
     u32x4 *xs = reinterpret_cast<u32x4 *>(dyn_lds);
-    unsigned char *scr = dyn_lds + (async_x ? xb_bytes : 0);
+    unsigned char *scr = dyn_lds + (async_x ? xb_bytes : (size_t)early * 16);
     float *tw_lds = reinterpret_cast<float *>(
         dyn_lds + (async_x ? xb_bytes + scr_bytes : (xb_bytes > scr_bytes ? xb_bytes : scr_bytes)));
-    // Direct global -> LDS copy of the operand (one contiguous block, as the
-    // column stride equals the column count) by waves w0 .. w0 + nws - 1;
-    // lane l of a wave fills chunk i0 + l.
+    // Direct global -> LDS copy of operand chunks [c0, c1) (one contiguous
+    // block, as the column stride equals the column count) by waves
+    // w0 .. w0 + nws - 1; lane l of a wave fills chunk i0 + l.
     const uint16_t *xpart = p.xB + (size_t)u0 * kspu * 4 * cols * 8;  // the part's slice
-    auto stage_x = [&](int w0, int nws) {
+    auto stage_x = [&](int w0, int nws, int c0, int c1) {
         if (w < w0) return;
-        for (int i0 = (w - w0) * 64; i0 < nx; i0 += nws * 64)
-            if (i0 + lane < nx) load_lds16(xpart + (size_t)(i0 + lane) * 8, xs + i0);
+        for (int i0 = c0 + (w - w0) * 64; i0 < c1; i0 += nws * 64)
+            if (i0 + lane < c1) load_lds16(xpart + (size_t)(i0 + lane) * 8, xs + i0);
     };
 
     int nslots;
     if (FUSED) {
-        // the waves without a token in the routing's first pass issue the copy
-        if (async_x) {
+        // the waves without a token in the routing's first pass issue the
+        // chunks that do not overlap the routing scratch
+        if (early > 0) {
             if (T < kGuWaves)
-                stage_x(T, kGuWaves - T);
+                stage_x(T, kGuWaves - T, 0, early);
             else
-                stage_x(0, kGuWaves);
+                stage_x(0, kGuWaves, 0, early);
         }
         // routing, recomputed by every workgroup (bit-identical results)
         block_route<kGuWaves * 64>(p, scr, sexp, tw_lds, &nslots_sh, blockIdx.x == 0);
         nslots = nslots_sh;
-        if (!async_x) stage_x(0, kGuWaves);
+        if (early < nx) stage_x(0, kGuWaves, early, nx);
     } else {
         nslots = min(p.meta[1], p.max_slots);
         for (int i = threadIdx.x; i < nslots; i += kGuWaves * 64)
             sexp[i] = min(max(p.slot_expert[i], 0), p.has_shared ? E : E - 1);
-        stage_x(0, kGuWaves);
+        stage_x(0, kGuWaves, 0, nx);
     }
     wait_vm_all();
     __syncthreads();

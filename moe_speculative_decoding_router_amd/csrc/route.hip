@@ -17,15 +17,19 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Router GEMV: logits[t, e] = sum_h x[t, h] * Wr[e, h] in float32.
-// One workgroup per expert; its 4 waves split H; the partial sums are added
-// in a fixed order, so the result is reproducible.  The same kernel writes
+// One workgroup per expert; its 8 waves split H (at the Qwen3 and DeepSeek
+// widths every load of a wave is issued before any is used: one memory round
+// trip); the partial sums are added in a fixed order, so the result is
+// reproducible.  The same kernel writes
 // x as the bf16 matrix-core operand (high/low pair or single) for the FFN.
 // ---------------------------------------------------------------------------
-constexpr int kRouterThreads = 256;
+constexpr int kRouterThreads = 512;
+constexpr int kRouterWaves = kRouterThreads / 64;
 
-template <bool VEC4>
+// TC: tokens per pass (T itself up to 8, so no row is loaded twice).
+template <bool VEC4, int TC>
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) {
-    __shared__ float red[4][8];
+    __shared__ float red[kRouterWaves][8];
     const int e = blockIdx.x;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int H = p.H, T = p.T;
@@ -41,28 +45,28 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) 
 
     if (e < p.E) {
         const int n = VEC4 ? H / 4 : H;
-        const int hb = (w * n) / 4, he = ((w + 1) * n) / 4;
-        for (int t0 = 0; t0 < T; t0 += 8) {
-            float acc[8];
+        const int hb = (w * n) / kRouterWaves, he = ((w + 1) * n) / kRouterWaves;
+        for (int t0 = 0; t0 < T; t0 += TC) {
+            float acc[TC];
 #pragma unroll
-            for (int tt = 0; tt < 8; ++tt) acc[tt] = 0.f;
+            for (int tt = 0; tt < TC; ++tt) acc[tt] = 0.f;
             if (VEC4) {
                 // 4 float4 of Wr and of each token's x per lane per pass; all
                 // loads (clamped into range) are issued before any is used
                 const float4 *wr = reinterpret_cast<const float4 *>(p.Wr) + (size_t)e * n;
                 const float4 *xv = reinterpret_cast<const float4 *>(p.x);
-                const int nt = T - t0 < 8 ? T - t0 : 8;
+                const int nt = T - t0 < TC ? T - t0 : TC;
                 for (int h0 = hb + lane; h0 < he; h0 += 256) {
-                    float4 a[4], b[8][4];
+                    float4 a[4], b[TC][4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) a[u] = wr[min(h0 + 64 * u, he - 1)];
 #pragma unroll
-                    for (int tt = 0; tt < 8; ++tt)
+                    for (int tt = 0; tt < TC; ++tt)
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
                             b[tt][u] = xv[(size_t)(t0 + min(tt, nt - 1)) * n + min(h0 + 64 * u, he - 1)];
 #pragma unroll
-                    for (int tt = 0; tt < 8; ++tt)
+                    for (int tt = 0; tt < TC; ++tt)
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
                             if (tt < nt && h0 + 64 * u < he)
@@ -74,13 +78,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) 
                 for (int h = hb + lane; h < he; h += 64) {
                     const float a = wr[h];
 #pragma unroll
-                    for (int tt = 0; tt < 8; ++tt)
+                    for (int tt = 0; tt < TC; ++tt)
                         if (t0 + tt < T) acc[tt] += a * p.x[(size_t)(t0 + tt) * H + h];
                 }
             }
-            const int nt = T - t0 < 8 ? T - t0 : 8;
+            const int nt = T - t0 < TC ? T - t0 : TC;
 #pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
+            for (int tt = 0; tt < TC; ++tt) {
                 if (tt < nt) {
                     const float v = wave_sum(acc[tt]);
                     if (lane == 0) red[w][tt] = v;
@@ -89,7 +93,10 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) 
             __syncthreads();
             if (threadIdx.x < nt) {
                 const int tt = threadIdx.x;
-                p.logits[(size_t)(t0 + tt) * p.E + e] = ((red[0][tt] + red[1][tt]) + red[2][tt]) + red[3][tt];
+                float sum = red[0][tt];
+#pragma unroll
+                for (int q = 1; q < kRouterWaves; ++q) sum += red[q][tt];
+                p.logits[(size_t)(t0 + tt) * p.E + e] = sum;
             }
             __syncthreads();
         }
@@ -126,8 +133,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(VerifyParams p) {
 }  // namespace
 
 hipError_t launch_router(const VerifyParams &p, hipStream_t s, KernelEvents ev) {
-    if (p.H % 4 == 0) return launch_k(router_kernel<true>, dim3(p.E), dim3(kRouterThreads), 0, s, ev, p);
-    return launch_k(router_kernel<false>, dim3(p.E), dim3(kRouterThreads), 0, s, ev, p);
+    const dim3 g(p.E), b(kRouterThreads);
+    if (p.H % 4 != 0) return launch_k(router_kernel<false, 8>, g, b, 0, s, ev, p);
+    switch (p.T < 8 ? p.T : 8) {
+        case 1: return launch_k(router_kernel<true, 1>, g, b, 0, s, ev, p);
+        case 2: return launch_k(router_kernel<true, 2>, g, b, 0, s, ev, p);
+        case 3: return launch_k(router_kernel<true, 3>, g, b, 0, s, ev, p);
+        case 4: return launch_k(router_kernel<true, 4>, g, b, 0, s, ev, p);
+        case 5: return launch_k(router_kernel<true, 5>, g, b, 0, s, ev, p);
+        case 6: return launch_k(router_kernel<true, 6>, g, b, 0, s, ev, p);
+        case 7: return launch_k(router_kernel<true, 7>, g, b, 0, s, ev, p);
+        default: return launch_k(router_kernel<true, 8>, g, b, 0, s, ev, p);
+    }
 }
 
 size_t route_lds_bytes(const VerifyParams &p) { return RouteScratch::bytes(p.T, p.k, p.E, kRouteThreads / 64); }

@@ -242,7 +242,7 @@ struct RouteScratch {
     int *misc;                  // [4]: U, |P*|
 
     __host__ __device__ static size_t bytes(int T, int k, int E, int waves) {
-        return (size_t)waves * 2 * kRankSlots * sizeof(RankEntry) + (size_t)E * 8 + (size_t)T * kTokWords * 8 +
+        return (size_t)waves * 2 * kRankSlots * sizeof(RankEntry) + (((size_t)E * 8 + 15) & ~(size_t)15) + (size_t)T * kTokWords * 8 +
                (size_t)T * k * 16 + (size_t)E * 8 + (size_t)T * 4 + (size_t)(2 * waves + 4) * 4 + 64;
     }
     __device__ void carve(unsigned char *base, int T, int k, int E, int waves) {
@@ -250,7 +250,7 @@ struct RouteScratch {
         rank = reinterpret_cast<RankEntry *>(q);
         q += (size_t)waves * 2 * kRankSlots * sizeof(RankEntry);
         tmask = reinterpret_cast<unsigned long long *>(q);
-        q += (size_t)E * 8;
+        q += ((size_t)E * 8 + 15) & ~(size_t)15;  // tbits rows are read 16 bytes at a time
         tbits = reinterpret_cast<unsigned *>(q);
         q += (size_t)T * kTokWords * 4;
         tbits0 = reinterpret_cast<unsigned *>(q);
@@ -441,14 +441,36 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     int *slot_off = reinterpret_cast<int *>(sh.g);  // g is free again: CSR offset per slot
     if (w == 0) {
         const unsigned long long below = (1ull << lane) - 1ull;
+        // token masks of this lane's experts (lane + 64 j): the words of 8
+        // token rows at a time are read with 16-byte broadcast loads that are
+        // all in flight together; expert e sits in word e / 32 = 2 j + lane / 32
+        constexpr int NQ = (NJ + 1) / 2;  // 16-byte loads per row (words 0 .. 2 NJ - 1)
+        const int hi = lane >> 5;
+        unsigned long long mskj[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) mskj[j] = 0ull;
+        for (int t0 = 0; t0 < T; t0 += 8) {
+            u32x4 rw[8][NQ];
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    rw[tt][q] = t0 + tt < T ? reinterpret_cast<const u32x4 *>(sh.tbits + (t0 + tt) * kTokWords)[q]
+                                            : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const u32x4 v = rw[tt][j >> 1];
+                    const unsigned word = (j & 1) ? (hi ? v.w : v.z) : (hi ? v.y : v.x);
+                    mskj[j] |= (unsigned long long)((word >> (lane & 31)) & 1u) << (t0 + tt);
+                }
+        }
         int base_r = 0, base_c = 0;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int e = lane + 64 * j;
-            unsigned long long msk = 0ull;
-            if (e < E)
-                for (int t = 0; t < T; ++t)
-                    msk |= (unsigned long long)((sh.tbits[t * kTokWords + (e >> 5)] >> (e & 31)) & 1u) << t;
+            const unsigned long long msk = e < E ? mskj[j] : 0ull;
             const int cnt = __popcll(msk);
             const unsigned long long bal = __ballot(cnt > 0);
             const int incl = wave_incl_scan(cnt);
