@@ -501,7 +501,12 @@ constexpr int kDnWaves = 8;
 
 template <int WT, int NT>
 struct DnCfg {
-    static constexpr int RG = NT <= 2 || (WT == 0 && NT == 3) ? 2 : 1;    // row tiles per unit
+    // row tiles per unit: sharing the activation fragment over 2 row tiles
+    // halves its L2 reads, which pays where the fragment is large (fp8: 4
+    // k-steps per unit; bf16 with more than 16 columns); for bf16 with one
+    // column tile the L2 reads are cheap and single row tiles balance better
+    // (whole row tiles per workgroup at H = 4096, fewer pieces elsewhere)
+    static constexpr int RG = (WT == 0 && NT == 1) ? 1 : (NT <= 2 || (WT == 0 && NT == 3) ? 2 : 1);
     static constexpr int KT = WT == 1 ? 64 : 32;                          // k per packed tile
     static constexpr int NA = WT == 1 ? 2 : 1;                            // tile loads per row tile
     static constexpr int NS = WT == 1 ? 4 : 1;                            // k-steps per unit
