@@ -17,8 +17,8 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Router GEMV: logits[t, e] = sum_h x[t, h] * Wr[e, h] in float32.
-// One workgroup per expert; its 8 waves split H (at the Qwen3 and DeepSeek
-// widths every load of a wave is issued before any is used: one memory round
+// One workgroup per expert; its 8 waves split H (every load of a wave is
+// issued before any is used, up to 20 tokens in one pass: one memory round
 // trip); the partial sums are added in a fixed order, so the result is
 // reproducible.  The same kernel writes
 // x as the bf16 matrix-core operand (high/low pair or single) for the FFN.
@@ -26,10 +26,12 @@ namespace {
 constexpr int kRouterThreads = 512;
 constexpr int kRouterWaves = kRouterThreads / 64;
 
-// TC: tokens per pass (T itself up to 8, so no row is loaded twice).
-template <bool VEC4, int TC>
+// TC: tokens per pass (T itself when it fits, so no row is loaded twice and
+// up to 20 tokens take one pass); UP: float4 of the row per lane and pass
+// (2 covers H <= 4096 with 8 waves, 4 covers H <= 8192).
+template <bool VEC4, int TC, int UP>
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) {
-    __shared__ float red[kRouterWaves][8];
+    __shared__ float red[kRouterWaves][TC];
     const int e = blockIdx.x;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int H = p.H, T = p.T;
@@ -51,24 +53,24 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) 
 #pragma unroll
             for (int tt = 0; tt < TC; ++tt) acc[tt] = 0.f;
             if (VEC4) {
-                // 4 float4 of Wr and of each token's x per lane per pass; all
+                // UP float4 of Wr and of each token's x per lane per pass; all
                 // loads (clamped into range) are issued before any is used
                 const float4 *wr = reinterpret_cast<const float4 *>(p.Wr) + (size_t)e * n;
                 const float4 *xv = reinterpret_cast<const float4 *>(p.x);
                 const int nt = T - t0 < TC ? T - t0 : TC;
-                for (int h0 = hb + lane; h0 < he; h0 += 256) {
-                    float4 a[4], b[TC][4];
+                for (int h0 = hb + lane; h0 < he; h0 += 64 * UP) {
+                    float4 a[UP], b[TC][UP];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) a[u] = wr[min(h0 + 64 * u, he - 1)];
+                    for (int u = 0; u < UP; ++u) a[u] = wr[min(h0 + 64 * u, he - 1)];
 #pragma unroll
                     for (int tt = 0; tt < TC; ++tt)
 #pragma unroll
-                        for (int u = 0; u < 4; ++u)
+                        for (int u = 0; u < UP; ++u)
                             b[tt][u] = xv[(size_t)(t0 + min(tt, nt - 1)) * n + min(h0 + 64 * u, he - 1)];
 #pragma unroll
                     for (int tt = 0; tt < TC; ++tt)
 #pragma unroll
-                        for (int u = 0; u < 4; ++u)
+                        for (int u = 0; u < UP; ++u)
                             if (tt < nt && h0 + 64 * u < he)
                                 acc[tt] += a[u].x * b[tt][u].x + a[u].y * b[tt][u].y + a[u].z * b[tt][u].z +
                                            a[u].w * b[tt][u].w;
@@ -117,11 +119,11 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// Route as its own launch (one workgroup of 1024 threads); used when the
+// Route as its own launch (one workgroup of 512 threads); used when the
 // gate-up kernel cannot hold the routing tables in LDS, and for float32
 // weights.  The tables go to the workspace for the FFN kernels.
 // ---------------------------------------------------------------------------
-constexpr int kRouteThreads = 1024;
+constexpr int kRouteThreads = 512;  // one thread per expert at the most experts; 256 registers per lane
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(VerifyParams p) {
     extern __shared__ __align__(16) unsigned char dyn[];
@@ -130,21 +132,35 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(VerifyParams p) {
     block_route<kRouteThreads>(p, dyn, p.slot_expert, p.tokw, &nslots, true);
 }
 
+template <int UP>
+hipError_t launch_router_up(const VerifyParams &p, hipStream_t s, KernelEvents ev) {
+    const dim3 g(p.E), b(kRouterThreads);
+    // tokens per pass: T up to 8 exactly, else 10 or (with 2 float4 per lane)
+    // 20, keeping the operand registers of a pass near 160
+    const int T = p.T;
+    const int tc = T <= 8 ? T : (T <= 10 || UP > 2 ? 10 : 20);
+    switch (tc) {
+        case 1: return launch_k(router_kernel<true, 1, UP>, g, b, 0, s, ev, p);
+        case 2: return launch_k(router_kernel<true, 2, UP>, g, b, 0, s, ev, p);
+        case 3: return launch_k(router_kernel<true, 3, UP>, g, b, 0, s, ev, p);
+        case 4: return launch_k(router_kernel<true, 4, UP>, g, b, 0, s, ev, p);
+        case 5: return launch_k(router_kernel<true, 5, UP>, g, b, 0, s, ev, p);
+        case 6: return launch_k(router_kernel<true, 6, UP>, g, b, 0, s, ev, p);
+        case 7: return launch_k(router_kernel<true, 7, UP>, g, b, 0, s, ev, p);
+        case 8: return launch_k(router_kernel<true, 8, UP>, g, b, 0, s, ev, p);
+        case 10: return launch_k(router_kernel<true, 10, UP>, g, b, 0, s, ev, p);
+        default: return launch_k(router_kernel<true, 20, 2>, g, b, 0, s, ev, p);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_router(const VerifyParams &p, hipStream_t s, KernelEvents ev) {
-    const dim3 g(p.E), b(kRouterThreads);
-    if (p.H % 4 != 0) return launch_k(router_kernel<false, 8>, g, b, 0, s, ev, p);
-    switch (p.T < 8 ? p.T : 8) {
-        case 1: return launch_k(router_kernel<true, 1>, g, b, 0, s, ev, p);
-        case 2: return launch_k(router_kernel<true, 2>, g, b, 0, s, ev, p);
-        case 3: return launch_k(router_kernel<true, 3>, g, b, 0, s, ev, p);
-        case 4: return launch_k(router_kernel<true, 4>, g, b, 0, s, ev, p);
-        case 5: return launch_k(router_kernel<true, 5>, g, b, 0, s, ev, p);
-        case 6: return launch_k(router_kernel<true, 6>, g, b, 0, s, ev, p);
-        case 7: return launch_k(router_kernel<true, 7>, g, b, 0, s, ev, p);
-        default: return launch_k(router_kernel<true, 8>, g, b, 0, s, ev, p);
-    }
+    if (p.H % 4 != 0)
+        return launch_k(router_kernel<false, 8, 1>, dim3(p.E), dim3(kRouterThreads), 0, s, ev, p);
+    // float4 of the row per wave: 2 per lane cover up to 128
+    const int per_wave = (p.H / 4 + kRouterWaves - 1) / kRouterWaves;
+    return per_wave <= 128 ? launch_router_up<2>(p, s, ev) : launch_router_up<4>(p, s, ev);
 }
 
 size_t route_lds_bytes(const VerifyParams &p) { return RouteScratch::bytes(p.T, p.k, p.E, kRouteThreads / 64); }
