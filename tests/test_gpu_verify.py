@@ -95,6 +95,25 @@ def test_exact_ties_and_k_equals_E():
     assert out["union_size"][0] == 8
 
 
+@pytest.mark.parametrize("bias_on", [False, True])
+def test_f32_route_kernel_max_experts(bias_on):
+    """Float32 weights route in the standalone route kernel: E = 512 experts
+    (8 entries per lane), k = 32 (radix selection; k + 1 with the bias),
+    T = 9."""
+    log(f"case f32 E=512 k=32 T=9 bias={bias_on}")
+    rng = np.random.default_rng(77)
+    T, H, I, E, k = 9, 64, 32, 512, 32
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    Wr = (0.5 * rng.standard_normal((E, H))).astype(np.float32)
+    Wgu = (0.05 * rng.standard_normal((E, 2 * I, H))).astype(np.float32)
+    Wd = (0.05 * rng.standard_normal((E, H, I))).astype(np.float32)
+    bias = (64, 0.5, rng.random(T).astype(np.float32)) if bias_on else None
+    out = run_layer(f32_layer(Wr, Wgu, Wd, k), x, bias)
+    r = check_routing(out, k, E, bias, x, Wr)
+    y_ref = omoe.moe_layer(x, r.topk_idx, r.topk_w, f32_expert_fn(Wgu, Wd, I))
+    check_output(out, y_ref, "f32", split=True)
+
+
 SMALL_BF16 = dict(H=512, I=384, E=32, k=4, rate=0.05, cid=10)
 
 
