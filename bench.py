@@ -183,6 +183,8 @@ def main() -> int:
 
     out_extra = {"read_stream": read_stream(m, torch, dev),
                  "select_4096_trees": select_timing(m, synth, wl, dev, stream, nt=4096)}
+    if wl.n_seq > 1:
+        out_extra["config_ab"] = config_ab(m, synth, wl, layers, dev)
 
     # ---------------- CPU oracle baseline (bounded sample) ----------------
     cpu = None
@@ -370,6 +372,60 @@ def read_stream(m, torch, dev, gib=4, reps=10):
     err(f"[bench] read stream (moe_stream_read, {gib} GiB): {gbs:.0f} GB/s")
     return {"GBs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "kernel": f"read_probe_kernel (moe_stream_read) over {gib} GiB, best of {reps}"}
+
+
+def config_ab(m, synth, wl, layers, dev, reps=15):
+    """The batched workload's A/B runs on the same expert weights, each layer
+    with the router planted for the arm's tokens: width against depth at
+    T = 2 ([W-vs-D] section 1: two consecutive tokens of one sequence, whose
+    routes are correlated, against one token from each of two sequences) and
+    the reuse bias off and on at the workload's T ([S2-MoE] component 2,
+    cap 2k, alpha 0.5).  Reports unique experts and the verify kernel time
+    (router + gate-up + down events, median of reps calls) per layer."""
+    import dataclasses
+    import numpy as np
+    import torch
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def arm(T, n_seq, with_bias):
+        U, us = [], []
+        for l, (lw, _) in enumerate(layers):
+            x, _, Wr = synth.layer_inputs(wl, l, T=T, n_seq=n_seq)
+            lw2 = dataclasses.replace(lw, Wr=to_dev(Wr))
+            xd = to_dev(x)
+            bias = None
+            if with_bias:
+                rng = synth.rng_for(0, wl.cid, 999)
+                bias = m.Bias(cap=2 * wl.k, alpha=0.5, w_conf=to_dev(rng.random(T).astype(np.float32)))
+            ws = m.alloc_workspace(lw2, T, bias, device=dev)
+            y = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
+            m.verify_layer(xd, lw2, bias, out=y, workspace=ws)
+            torch.cuda.synchronize()
+            U.append(int(ws.aux.union_size.item()))
+            times = []
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * m.NUM_STAGES)]
+            for e in ev:  # torch creates the HIP event at its first record
+                e.record()
+            torch.cuda.synchronize()
+            for _ in range(reps):
+                m.verify_layer(xd, lw2, bias, out=y, workspace=ws, events=ev)
+                torch.cuda.synchronize()
+                times.append(sum(ev[2 * q].elapsed_time(ev[2 * q + 1]) for q in (0, 2, 3)) * 1e3)
+            us.append(float(np.median(times)))
+        return {"unique_experts_per_layer": round(float(np.mean(U)), 2),
+                "verify_kernel_us_per_layer": round(float(np.mean(us)), 1), "unions": U}
+
+    res = {"width_vs_depth_T2": {"depth_one_sequence": arm(2, 1, False), "width_two_sequences": arm(2, 2, False)},
+           "reuse_bias": {"off": arm(wl.T, wl.n_seq, False), "on": arm(wl.T, wl.n_seq, True)}}
+    wd, rb = res["width_vs_depth_T2"], res["reuse_bias"]
+    err(f"[bench] T=2 depth: U {wd['depth_one_sequence']['unique_experts_per_layer']}, "
+        f"{wd['depth_one_sequence']['verify_kernel_us_per_layer']} us; width: U "
+        f"{wd['width_two_sequences']['unique_experts_per_layer']}, {wd['width_two_sequences']['verify_kernel_us_per_layer']} us")
+    err(f"[bench] bias off: U {rb['off']['unique_experts_per_layer']}, {rb['off']['verify_kernel_us_per_layer']} us; "
+        f"on: U {rb['on']['unique_experts_per_layer']}, {rb['on']['verify_kernel_us_per_layer']} us")
+    return res
 
 
 def select_timing(m, synth, wl, dev, stream, nt=4096, reps=20):
