@@ -4,22 +4,29 @@
 // layer the verified tokens need the weights of the union of their experts;
 // each unique expert is loaded once and applied to all of its tokens).
 //
-// Work decomposition (bf16 / fp8 weights):
-//   gate-up : item = (union slot s, 16 intermediate rows i0..i0+15).  The 4
-//             waves of a workgroup split the H contraction; each streams the
-//             16 gate rows and 16 up rows of its K-quarter with 16-byte
-//             non-temporal loads straight into the matrix-core A operand
-//             (v_mfma_f32_16x16x32_bf16; fp8 is decoded exactly to bf16 in
-//             registers and each 128-wide K block is scaled after its own
-//             products).  The activations are the B operand: the T tokens as
-//             columns (as a bf16 high/low pair when 2T <= 64), read from a
-//             small L2-resident buffer.  Partial sums meet in LDS in a fixed
+// Work decomposition (bf16 / fp8 weights, one workgroup of 8 waves per
+// compute unit):
+//   gate-up : the routing runs in every workgroup's prologue (route_block.h).
+//             Item = (union slot, 16 packed rows: 8 gate + 8 up rows of the
+//             same intermediate indices).  Items go round-robin to the
+//             workgroups (the tail by tickets when the activation operand is
+//             read from L2); the 8 waves take interleaved batches of the
+//             item's contraction, streaming packed 1 KB tiles with 16-byte
+//             non-temporal loads straight into the A operand of
+//             v_mfma_f32_16x16x32_bf16 (fp8 is decoded exactly to bf16 in
+//             registers, each 128-wide block scaled after its products).  The
+//             activations are the B operand, staged once per workgroup in
+//             LDS: the T tokens as columns, as a bf16 high/low pair when
+//             2T <= 16.  When the operand does not fit in LDS the contraction
+//             of each item is split over 2 or 4 workgroups and a SwiGLU
+//             combine kernel finishes it.  Partial sums meet in LDS in a fixed
 //             order; SiLU(gate) * up, times the token's gate weight, is
 //             written in the B-operand layout of the down projection.
-//   down    : one workgroup per 16 output rows; its waves split the I
-//             contraction and stream that row tile of every union slot, so y
-//             is accumulated in registers over all experts and written once
-//             (deterministic, no atomics, equal bytes per workgroup).
+//   down    : units (row group, slot, k-unit) split evenly over the
+//             workgroups (stream-K); a workgroup owning a whole row group
+//             writes y, shared row groups exchange pieces through the
+//             workspace and the last to finish adds them in workgroup order.
+//             No atomics on y: the result does not depend on timing.
 // Float32 weights use plain VALU dot products (one wave per output row),
 // per-(token, expert) rows of ydown and a combine in rank order.
 #include <math.h>
