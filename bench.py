@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the workload, copy this many MiB device to device once (a plain copy of "
                          "known size, the calibration of the HBM byte counters)")
+    ap.add_argument("--no-ab", action="store_true",
+                    help="skip the batched workload's width/depth and bias A/B runs (profiling runs)")
     ap.add_argument("--ablation", action="store_true",
                     help="also run the EcoSpec gamma sweep and static-cost ablation (field 'ablation')")
     return ap.parse_args()
@@ -183,7 +185,7 @@ def main() -> int:
 
     out_extra = {"read_stream": read_stream(m, torch, dev),
                  "select_4096_trees": select_timing(m, synth, wl, dev, stream, nt=4096)}
-    if wl.n_seq > 1:
+    if wl.n_seq > 1 and not args.no_ab:
         out_extra["config_ab"] = config_ab(m, synth, wl, layers, dev)
 
     # ---------------- CPU oracle baseline (bounded sample) ----------------
