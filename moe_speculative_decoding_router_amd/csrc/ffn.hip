@@ -305,6 +305,19 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
             else
                 stage_x(0, kGuWaves, 0, early);
         }
+        // An always-on shared expert is slot 0, so this workgroup's first
+        // item is its row tile b (while b < rtiles) whatever the routing
+        // gives: the waves without a token pull the first half of that
+        // item's tiles into L2 during the routing (direct loads into a
+        // scratch block of the reduction buffer, which the main loop
+        // overwrites later), and that half then streams from L2.  (The whole
+        // item, about the size of an XCD's L2 over its 32 workgroups, is
+        // mostly evicted before use; half of it gained most: 2.6 us per
+        // DeepSeek gate-up against 0.6 for the whole and 1.9 for a quarter.)
+        if (KS == 1 && p.has_shared && (int)blockIdx.x < rtiles && T < kGuWaves && w >= T) {
+            const uint8_t *sht = static_cast<const uint8_t *>(p.Wsh_gu) + (size_t)blockIdx.x * nkt * 1024 + lane * 16;
+            for (int c = w - T; c < nkt / 2; c += kGuWaves - T) load_lds16(sht + (size_t)c * 1024, &red[0][w][0][0]);
+        }
         // routing, recomputed by every workgroup (bit-identical results)
         block_route<kGuWaves * 64>(p, scr, sexp, tw_lds, &nslots_sh, blockIdx.x == 0);
         nslots = nslots_sh;

@@ -276,7 +276,8 @@ struct RouteScratch {
 };
 
 // Routes the call with NTHREADS threads (NTHREADS >= E).  Results:
-//   LDS: sexp[s] expert of slot s (E = shared expert), tw[s * T + t] gate
+//   LDS: sexp[s] expert of slot s (slot 0 = the shared expert E when there
+//        is one, then the union in ascending order), tw[s * T + t] gate
 //        weight of token t in slot s (0 if not routed), *nslots_lds.
 //   global (when write_global): topk_idx, topk_w, union, CSR, P* (ascending),
 //        meta, the slot tables (slot_expert, tokw, tokpos, tpos) of the FFN
@@ -437,8 +438,10 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     }
 
     // ---- union (ascending) and CSR row offsets: wave 0 scans the experts,
-    //      NJ groups of 64; slot = rank in the union ----
-    int *slot_off = reinterpret_cast<int *>(sh.g);  // g is free again: CSR offset per slot
+    //      NJ groups of 64; slot = rank in the union, after the always-on
+    //      shared expert (slot 0) when there is one ----
+    const int so = p.has_shared ? 1 : 0;
+    int *slot_off = reinterpret_cast<int *>(sh.g);  // g is free again: CSR offset per union rank
     if (w == 0) {
         const unsigned long long below = (1ull << lane) - 1ull;
         // token masks of this lane's experts (lane + 64 j): the words of 8
@@ -477,13 +480,13 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
             if (cnt > 0) {
                 const int rank = base_r + __popcll(bal & below);
                 const int off = base_c + incl - cnt;
-                sexp[rank] = e;
+                sexp[rank + so] = e;
                 slot_off[rank] = off;
                 sh.tmask[e] = msk;
                 if (write_global) {
                     p.union_experts[rank] = e;
                     p.csr_ptr[rank] = off;
-                    p.slot_expert[rank] = e;
+                    p.slot_expert[rank + so] = e;
                 }
             }
             base_r += __popcll(bal);
@@ -497,7 +500,8 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     //      entry written once ----
     const int U = sh.misc[0];
     for (int i = tid; i < U * T; i += NTHREADS) {
-        const int s = i / T, t = i - s * T;
+        const int r = i / T, t = i - r * T;  // union rank, token
+        const int s = r + so;                // slot
         const int e = sexp[s];
         const unsigned long long msk = sh.tmask[e];
         float wt = 0.f;
@@ -507,7 +511,7 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
             for (int j = 0; j < k; ++j)
                 if (sh.fin_i[t * k + j] == e) jj = j;
             wt = sh.fin_w[t * k + jj];
-            pos = slot_off[s] + __popcll(msk & ((1ull << t) - 1ull));
+            pos = slot_off[r] + __popcll(msk & ((1ull << t) - 1ull));
             if (write_global) {
                 p.csr_tok[pos] = t;
                 p.csr_w[pos] = wt;
@@ -520,13 +524,13 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
             p.tokpos[(size_t)s * T + t] = pos;
         }
     }
-    if (p.has_shared && tid < T) {
-        if (tid == 0) sexp[U] = E;
-        tw[U * T + tid] = 1.f;
+    if (p.has_shared && tid < T) {  // slot 0: the shared expert, weight 1 for every token
+        if (tid == 0) sexp[0] = E;
+        tw[tid] = 1.f;
         if (write_global) {
-            if (tid == 0) p.slot_expert[U] = E;
-            p.tokw[(size_t)U * T + tid] = 1.f;
-            p.tokpos[(size_t)U * T + tid] = T * k + tid;
+            if (tid == 0) p.slot_expert[0] = E;
+            p.tokw[tid] = 1.f;
+            p.tokpos[tid] = T * k + tid;
         }
     }
     if (tid == 0) {
