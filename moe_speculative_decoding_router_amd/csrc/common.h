@@ -110,6 +110,14 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
 }
 
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l of the wave writes lds_wave_base + 16 l;
+// the base must be the same in every lane.  Completion is tracked by the
+// vector memory counter, so a wait for it and a barrier precede any read.
+__device__ __forceinline__ void load_lds16(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS (and
 // scalar) operations, not for its outstanding global loads, so direct
 // global->LDS loads issued earlier stay in flight across it.  __syncthreads()

@@ -42,13 +42,6 @@ constexpr int kFfnThreads = 256;
 constexpr int kGateUpWgPerCu = 1;  // persistent workgroups per CU (8 waves each)
 constexpr size_t kLdsPerCu = 160 * 1024;      // LDS of one gfx950 compute unit
 
-// 16 bytes per lane from global memory straight into LDS
-// (global_load_lds_dwordx4): lane l of the wave writes lds_wave_base + 16 l;
-// the base must be the same in every lane.  Completion is tracked by the
-// vector memory counter, so wait_vm_all() and a barrier precede any read.
-__device__ __forceinline__ void load_lds16(const void *src, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
-}
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ u32x4 ld_nt(const uint8_t *ptr) {
