@@ -6,7 +6,9 @@
  *   [EcoSpec] review of "Less Experts, Faster Decoding: Cost-Aware Speculative
  *             Decoding for Mixture-of-Experts";
  *   [S2-MoE]  walkthrough of S^2-MoE (self-speculative decoding for MoE on
- *             edge devices).
+ *             edge devices);
+ *   [W-vs-D]  summary of the width-vs-depth article (batch versus
+ *             speculation for MoE on one GPU).
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
