@@ -42,7 +42,16 @@ constexpr int kFfnThreads = 256;
 constexpr int kGateUpWgPerCu = 1;  // persistent workgroups per CU (8 waves each)
 constexpr size_t kLdsPerCu = 160 * 1024;      // LDS of one gfx950 compute unit
 
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits for every vector memory access of this wave (vmcnt(0); expcnt and
+// lgkmcnt left at their maxima).  Issued through the builtin so that the
+// compiler's wait insertion knows the direct-to-LDS copies are complete and
+// adds no waits of its own to later LDS reads; the empty asm statements keep
+// memory accesses from moving across it.
+__device__ __forceinline__ void wait_vm_all() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ u32x4 ld_nt(const uint8_t *ptr) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ptr));
@@ -481,6 +490,11 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
         }
         return vv;
     };
+    // The loop leaves only at its end: an exit between the two halves would
+    // give the compiler a path to the loop head with the first half's loads
+    // still pending, and it would then wait for them at every iteration.
+    // After the last batch the second half re-loads that batch (its
+    // products are zeroed) and the loop ends.
     B b0, b1;
     load_batch(b0, 0);
     for (int f = 0;; f += 2) {
@@ -488,11 +502,10 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
         load_batch(b1, v1 ? f + 1 : f);
         compute_batch<WT, NT, KU>(b0, acc, true);
         if (f % nb == nb - 1) finish_item(acc, f);
-        if (!v1) break;
-        const bool v2 = valid_ord((f + 2) / nb);
-        load_batch(b0, v2 ? f + 2 : f + 1);
-        compute_batch<WT, NT, KU>(b1, acc, true);
-        if ((f + 1) % nb == nb - 1) finish_item(acc, f + 1);
+        const bool v2 = v1 && valid_ord((f + 2) / nb);
+        load_batch(b0, v2 ? f + 2 : (v1 ? f + 1 : f));
+        compute_batch<WT, NT, KU>(b1, acc, v1);
+        if (v1 && (f + 1) % nb == nb - 1) finish_item(acc, f + 1);
         if (!v2) break;
     }
 }
@@ -682,10 +695,15 @@ __global__ __launch_bounds__(kDnWaves * 64) void down_kernel(VerifyParams p) {
         if (nbw > 0) {
             B b0, b1;
             load_batch(b0, 0);
+            // the scheduling barriers keep each batch's loads issued before
+            // the products of the batch before it, so one batch is always in
+            // flight while the other is multiplied
             for (int f = 0; f < nbw; f += 2) {
                 load_batch(b1, min(f + 1, nbw - 1));
+                __builtin_amdgcn_sched_barrier(0);
                 dn_compute<WT, NT>(b0, acc, true);
                 load_batch(b0, min(f + 2, nbw - 1));
+                __builtin_amdgcn_sched_barrier(0);
                 dn_compute<WT, NT>(b1, acc, f + 1 < nbw);
             }
         }

@@ -175,6 +175,22 @@ def test_bf16_gptoss_contraction_tail():
     verify_workload(wl)
 
 
+@pytest.mark.parametrize("case", ["fp8_straddle", "bf16_multi_group"])
+def test_down_shared_row_groups(case):
+    """Down kernel with row groups shared between workgroups.  fp8 at
+    H = 2816 (88 row groups of 2 row tiles over one workgroup per CU): most
+    workgroups' ranges straddle two row groups and are streamed as one
+    window.  bf16 at H = 7168 (448 row groups): each workgroup owns one or
+    two whole row groups between two pieces, so a range spans two windows."""
+    if case == "fp8_straddle":
+        log("case fp8 H=2816 T=5 (down ranges straddle row groups)")
+        wl = small("deepseek_fp8", H=2816, I=256, E=16, k=4, T=5, shared=True, cid=16)
+    else:
+        log("case bf16 H=7168 T=5 (several row groups per down workgroup)")
+        wl = small("qwen3_bf16", H=7168, I=256, E=16, k=4, T=5, rate=0.05, cid=17)
+    verify_workload(wl)
+
+
 def test_deterministic_two_runs():
     log("case determinism")
     wl = small("qwen3_bf16", T=5, **SMALL_BF16)
