@@ -132,6 +132,33 @@ def test_bf16_small_with_bias(T):
     verify_workload(wl, bias_np=(8, 0.5, rng.random(T).astype(np.float32)))
 
 
+@pytest.mark.parametrize("T", [1, 5])
+def test_bf16_top1_routing(T):
+    """k = 1: one expert per token, gate weight exactly 1."""
+    log(f"case bf16 top-1 T={T}")
+    wl = small("qwen3_bf16", T=T, **{**SMALL_BF16, "k": 1})
+    out, _ = verify_workload(wl)
+    assert np.all(out["topk_w"] == 1.0)
+
+
+def test_identical_tokens_one_expert_set():
+    """Every token the same: the union is one token's k experts, and every
+    output row is the same bits (token columns never mix)."""
+    log("case bf16 identical tokens")
+    wl = small("qwen3_bf16", T=6, **SMALL_BF16)
+    x, _, Wr = synth.layer_inputs(wl, 0)
+    x = np.repeat(x[:1], wl.T, axis=0)
+    from gpu_helpers import device_layer, expert_fn_raw
+    lw = device_layer(wl, 0, Wr)
+    out = run_layer(lw, x)
+    r = check_routing(out, wl.k, wl.E, None, x, Wr)
+    assert int(out["union_size"][0]) == wl.k
+    y_ref = omoe.moe_layer(x, r.topk_idx, r.topk_w, expert_fn_raw(wl, 0))
+    check_output(out, y_ref, "bf16", split=2 * wl.T <= 16)
+    for t in range(1, wl.T):
+        assert np.array_equal(out["y"][t], out["y"][0]), t
+
+
 @pytest.mark.parametrize("E,k,bias", [(64, 20, False), (64, 16, True), (512, 8, False), (512, 32, True)])
 def test_bf16_wide_routing(E, k, bias):
     """Selections past 16 ranks (radix search) and 8 entries per lane (E = 512)."""
@@ -141,7 +168,7 @@ def test_bf16_wide_routing(E, k, bias):
     verify_workload(wl, bias_np=bias_np)
 
 
-@pytest.mark.parametrize("T,shared", [(5, True), (5, False), (12, True), (40, True)])
+@pytest.mark.parametrize("T,shared", [(1, True), (5, True), (5, False), (12, True), (40, True), (64, True)])
 def test_fp8_small(T, shared):
     log(f"case fp8 small T={T} shared={shared}")
     wl = small("deepseek_fp8", H=512, I=256, E=32, k=8, T=T, shared=shared, cid=11)
