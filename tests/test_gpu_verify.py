@@ -175,6 +175,20 @@ def test_fp8_small(T, shared):
     verify_workload(wl)
 
 
+def test_fp8_small_with_bias():
+    log("case fp8 small with bias T=5")
+    wl = small("deepseek_fp8", H=512, I=256, E=32, k=8, T=5, shared=True, cid=11)
+    verify_workload(wl, bias_np=(16, 0.5, np.random.default_rng(5).random(5).astype(np.float32)))
+
+
+def test_bf16_all_limits():
+    """E = 512, k = 32, T = 64 with the bias (cap 64): the largest routing
+    tables, the radix selection and up to 512 union slots in one call."""
+    log("case bf16 E=512 k=32 T=64 bias")
+    wl = small("qwen3_bf16", H=256, I=128, E=512, k=32, T=64, rate=0.05, cid=18)
+    verify_workload(wl, bias_np=(64, 0.5, np.random.default_rng(64).random(64).astype(np.float32)))
+
+
 @pytest.mark.parametrize("T", [20, 32, 64])
 def test_bf16_wide_operand(T):
     """H = 4096 with 20, 32 and 64 token columns: the activation operand does
