@@ -258,14 +258,24 @@ def alloc_workspace(layer: LayerWeights, T: int, bias: Optional[Bias] = None, de
 def verify_layer(x, layer: LayerWeights, bias: Optional[Bias] = None, *, out=None,
                  workspace: Optional[Workspace] = None, events: Optional[Sequence] = None, stream=None):
     """One MoE-layer verify step for x [T, H] float32 (device).  Returns
-    (y [T, H] float32, Aux or None)."""
+    (y [T, H] float32, Aux or None).  `stream`: a torch.cuda.Stream or a raw
+    hipStream_t handle (default: torch's current stream).  Buffers this call
+    allocates itself (workspace, y) come from the current stream's pool; on
+    another stream the launch first waits for the current stream, and the
+    buffers are marked as used by the launch stream."""
     import torch
     T = int(x.shape[0])
     if x.dtype != torch.float32 or x.dim() != 2 or x.shape[1] != layer.H or not x.is_contiguous():
         raise ValueError("x must be a contiguous float32 [T, H] tensor")
+    owned = []
     if workspace is None:
         workspace = alloc_workspace(layer, T, bias, device=x.device)
+        owned.append(workspace.ws)
+        if workspace.aux is not None:
+            owned += [getattr(workspace.aux, f) for f in Aux.__dataclass_fields__]
     y = out if out is not None else torch.empty_like(x)
+    if out is None:
+        owned.append(y)
     L = layer._c()
     b = bias._c() if bias is not None else None
     a = workspace.aux
@@ -277,7 +287,17 @@ def verify_layer(x, layer: LayerWeights, bias: Optional[Bias] = None, *, out=Non
                                                         for e in events])
     caux = _Aux(*([_ptr(getattr(a, f)) for f in Aux.__dataclass_fields__] if a else [None] * 10),
                 ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
-    s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+    cur = torch.cuda.current_stream(x.device)
+    if stream is None:
+        s = cur.cuda_stream
+    else:
+        sobj = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream),
+                                                                                             device=x.device)
+        s = sobj.cuda_stream
+        if owned and s != cur.cuda_stream:
+            sobj.wait_stream(cur)
+            for t in owned:
+                t.record_stream(sobj)
     rc = lib().moe_verify_layer(ctypes.byref(L), x.data_ptr(), T, ctypes.byref(b) if b else None, y.data_ptr(),
                                 ctypes.byref(caux), workspace.ws.data_ptr(), workspace.nbytes, s)
     _check(rc)

@@ -244,6 +244,26 @@ def test_deterministic_two_runs():
         assert np.array_equal(a[key], b[key]), key
 
 
+def test_side_stream_matches_current_stream():
+    """verify_layer launched on another stream (a torch.cuda.Stream, then its
+    raw handle), with the workspace and output allocated by the call: the
+    same bits as on the current stream."""
+    log("case side stream")
+    wl = small("qwen3_bf16", T=5, **SMALL_BF16)
+    x, _, Wr = synth.layer_inputs(wl, 0)
+    from gpu_helpers import device_layer
+    lw = device_layer(wl, 0, Wr)
+    xd = to_dev(x)
+    y0, a0 = m.verify_layer(xd, lw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    y1, a1 = m.verify_layer(xd, lw, stream=side)
+    y2, a2 = m.verify_layer(xd, lw, stream=side.cuda_stream)
+    side.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(y0, y2)
+    assert torch.equal(a0.topk_idx, a1.topk_idx) and torch.equal(a0.csr_tok, a2.csr_tok)
+
+
 @pytest.mark.parametrize("wdtype", ["bf16", "f32"])
 def test_stage_events_bracket_the_kernels(wdtype):
     """Per-stage start/end events: the kernels that run have positive
