@@ -146,6 +146,26 @@ class Bias:
         return _Bias(self.cap, self.alpha, _ptr(self.w_conf))
 
 
+def _launch_stream(stream, device, owned=()) -> int:
+    """Raw handle of the launch stream: torch's current stream when `stream`
+    is None, else a torch.cuda.Stream or a raw hipStream_t handle.  Tensors in
+    `owned` were allocated by the caller from the current stream's pool; on
+    another stream the launch first waits for the current stream (the memory
+    may still have pending uses there), and the tensors are marked as used
+    by the launch stream."""
+    import torch
+    cur = torch.cuda.current_stream(device)
+    if stream is None:
+        return cur.cuda_stream
+    sobj = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream), device=device)
+    owned = [t for t in owned if t is not None]
+    if owned and sobj.cuda_stream != cur.cuda_stream:
+        sobj.wait_stream(cur)
+        for t in owned:
+            t.record_stream(sobj)
+    return sobj.cuda_stream
+
+
 def pack_weights(src, wdtype: str, gate_up: bool, out=None, stream=None):
     """Pack row-major expert weights src [E, rows, K] (bf16 bits or fp8 codes,
     device) into the tile layout moe_verify_layer streams.  Returns the packed
@@ -157,7 +177,7 @@ def pack_weights(src, wdtype: str, gate_up: bool, out=None, stream=None):
         raise ValueError("src must be a contiguous [E, rows, K] tensor")
     E, rows, K = (int(v) for v in src.shape)
     dst = out if out is not None else torch.empty_like(src)
-    s = stream if stream is not None else torch.cuda.current_stream(src.device).cuda_stream
+    s = _launch_stream(stream, src.device, [dst] if out is None else [])
     _check(lib().moe_pack_weights(src.data_ptr(), dst.data_ptr(), E, rows, K, DTYPES[wdtype], int(bool(gate_up)), s))
     return dst
 
@@ -170,7 +190,7 @@ def stream_read(src, checksum, stream=None) -> None:
     if not src.is_contiguous():
         raise ValueError("src must be contiguous")
     nbytes = src.numel() * src.element_size()
-    s = stream if stream is not None else torch.cuda.current_stream(src.device).cuda_stream
+    s = _launch_stream(stream, src.device)
     _check(lib().moe_stream_read(src.data_ptr(), nbytes, checksum.data_ptr(), s))
 
 
@@ -287,17 +307,7 @@ def verify_layer(x, layer: LayerWeights, bias: Optional[Bias] = None, *, out=Non
                                                         for e in events])
     caux = _Aux(*([_ptr(getattr(a, f)) for f in Aux.__dataclass_fields__] if a else [None] * 10),
                 ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
-    cur = torch.cuda.current_stream(x.device)
-    if stream is None:
-        s = cur.cuda_stream
-    else:
-        sobj = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream),
-                                                                                             device=x.device)
-        s = sobj.cuda_stream
-        if owned and s != cur.cuda_stream:
-            sobj.wait_stream(cur)
-            for t in owned:
-                t.record_stream(sobj)
+    s = _launch_stream(stream, x.device, owned)
     rc = lib().moe_verify_layer(ctypes.byref(L), x.data_ptr(), T, ctypes.byref(b) if b else None, y.data_ptr(),
                                 ctypes.byref(caux), workspace.ws.data_ptr(), workspace.nbytes, s)
     _check(rc)
@@ -310,9 +320,14 @@ def union_stats(topk_idx, E: int, counts=None, reuse=None, stream=None):
     if topk_idx.dtype != torch.int32 or topk_idx.dim() != 3 or not topk_idx.is_contiguous():
         raise ValueError("topk_idx must be a contiguous int32 [nL, T, k] tensor")
     nL, T, k = (int(v) for v in topk_idx.shape)
-    counts = counts if counts is not None else torch.empty(nL, dtype=torch.int32, device=topk_idx.device)
-    reuse = reuse if reuse is not None else torch.empty(nL, dtype=torch.float32, device=topk_idx.device)
-    s = stream if stream is not None else torch.cuda.current_stream(topk_idx.device).cuda_stream
+    owned = []
+    if counts is None:
+        counts = torch.empty(nL, dtype=torch.int32, device=topk_idx.device)
+        owned.append(counts)
+    if reuse is None:
+        reuse = torch.empty(nL, dtype=torch.float32, device=topk_idx.device)
+        owned.append(reuse)
+    s = _launch_stream(stream, topk_idx.device, owned)
     _check(lib().union_stats(topk_idx.data_ptr(), nL, T, k, E, counts.data_ptr(), reuse.data_ptr(), s))
     return counts, reuse
 
@@ -333,7 +348,7 @@ def select_drafts(parent, P, Epred, gamma: int, eps: float = 1e-6, out=None, str
         raise ValueError("shape mismatch between parent, P and Epred")
     W = int(Epred.shape[2])
     S = out if out is not None else torch.empty((nt, gamma), dtype=torch.int32, device=P.device)
-    s = stream if stream is not None else torch.cuda.current_stream(P.device).cuda_stream
+    s = _launch_stream(stream, P.device, [S] if out is None else [])
     fn = lib().select_drafts_static if static else lib().select_drafts
     _check(fn(par.ctypes.data, N, P.data_ptr(), Epred.data_ptr(), W, gamma, eps, nt, S.data_ptr(), s))
     return S
@@ -359,7 +374,7 @@ def expand_drafts(parent, P, Epred, t_ar: float, t_exp: float, c_draft=None, str
     W = int(Epred.shape[2])
     S = torch.empty((nt, N), dtype=torch.int32, device=P.device)
     count = torch.empty((nt,), dtype=torch.int32, device=P.device)
-    s = stream if stream is not None else torch.cuda.current_stream(P.device).cuda_stream
+    s = _launch_stream(stream, P.device, [S, count])
     _check(lib().expand_drafts(par.ctypes.data, N, P.data_ptr(), Epred.data_ptr(), W, t_ar, t_exp,
                                c_draft.data_ptr() if c_draft is not None else None, nt, S.data_ptr(),
                                count.data_ptr(), s))
@@ -378,7 +393,7 @@ def union_stats_segments(topk_idx, E: int, offsets, stream=None):
     S = int(off.shape[0]) - 1
     per = torch.empty((nL, S), dtype=torch.int32, device=topk_idx.device)
     total = torch.empty((nL,), dtype=torch.int32, device=topk_idx.device)
-    s = stream if stream is not None else torch.cuda.current_stream(topk_idx.device).cuda_stream
+    s = _launch_stream(stream, topk_idx.device, [per, total])
     _check(lib().union_stats_segments(topk_idx.data_ptr(), nL, T, k, E, off.ctypes.data, S, per.data_ptr(),
                                       total.data_ptr(), s))
     return per, total
@@ -397,7 +412,7 @@ def gate_depths(c, Epred, t_base: float, t_exp: float, stream=None):
     if tuple(Epred.shape[:2]) != (S, D1):
         raise ValueError("shape mismatch between c and Epred")
     d = torch.empty((S,), dtype=torch.int32, device=c.device)
-    s = stream if stream is not None else torch.cuda.current_stream(c.device).cuda_stream
+    s = _launch_stream(stream, c.device, [d])
     _check(lib().gate_depths(c.data_ptr(), Epred.data_ptr(), S, D1 - 1, int(Epred.shape[2]), t_base, t_exp,
                              d.data_ptr(), s))
     return d

@@ -262,6 +262,12 @@ def test_side_stream_matches_current_stream():
     side.synchronize()
     assert torch.equal(y0, y1) and torch.equal(y0, y2)
     assert torch.equal(a0.topk_idx, a1.topk_idx) and torch.equal(a0.csr_tok, a2.csr_tok)
+    ti = a0.topk_idx.unsqueeze(0).contiguous()
+    c0, r0 = m.union_stats(ti, wl.E)
+    torch.cuda.synchronize()
+    c1, r1 = m.union_stats(ti, wl.E, stream=side)
+    side.synchronize()
+    assert torch.equal(c0, c1) and torch.equal(r0, r1) and int(c1[0]) == int(a0.union_size[0])
 
 
 @pytest.mark.parametrize("wdtype", ["bf16", "f32"])
