@@ -17,11 +17,12 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Router GEMV: logits[t, e] = sum_h x[t, h] * Wr[e, h] in float32.
-// One workgroup per expert; its 8 waves split H (every load of a wave is
-// issued before any is used, up to 20 tokens in one pass: one memory round
-// trip); the partial sums are added in a fixed order, so the result is
-// reproducible.  The same kernel writes
-// x as the bf16 matrix-core operand (high/low pair or single) for the FFN.
+// Workgroup (e, c) takes expert e and the c-th chunk of TC tokens (the
+// tokens are split so that the grid covers every compute unit even with
+// few experts); its 8 waves split H (every load of a wave is issued before
+// any is used: one memory round trip); the partial sums are added in a
+// fixed order, so the result is reproducible.  The same kernel writes x as
+// the bf16 matrix-core operand (high/low pair or single) for the FFN.
 // ---------------------------------------------------------------------------
 constexpr int kRouterThreads = 512;
 constexpr int kRouterWaves = kRouterThreads / 64;
@@ -36,7 +37,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int H = p.H, T = p.T;
     const int total = T * H;
-    const int gid = blockIdx.x * kRouterThreads + threadIdx.x, gstride = gridDim.x * kRouterThreads;
+    const int gid = (blockIdx.y * gridDim.x + blockIdx.x) * kRouterThreads + threadIdx.x;
+    const int gstride = gridDim.x * gridDim.y * kRouterThreads;
     // x element of the activation-operand conversion, loaded up front
     const bool conv = p.wdtype != 0;
     float xc = 0.f;
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) 
     if (e < p.E) {
         const int n = VEC4 ? H / 4 : H;
         const int hb = (w * n) / kRouterWaves, he = ((w + 1) * n) / kRouterWaves;
-        for (int t0 = 0; t0 < T; t0 += TC) {
+        for (int t0 = blockIdx.y * TC; t0 < T; t0 += TC * gridDim.y) {
             float acc[TC];
 #pragma unroll
             for (int tt = 0; tt < TC; ++tt) acc[tt] = 0.f;
@@ -132,13 +134,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(VerifyParams p) {
     block_route<kRouteThreads>(p, dyn, p.slot_expert, p.tokw, &nslots, true);
 }
 
+// Token chunks per expert: enough workgroups for the 256 compute units.
+int router_chunks(int E, int T) {
+    const int c = (256 + E - 1) / E;
+    return c < T ? c : T;
+}
+
 template <int UP>
 hipError_t launch_router_up(const VerifyParams &p, hipStream_t s, KernelEvents ev) {
-    const dim3 g(p.E), b(kRouterThreads);
-    // tokens per pass: T up to 8 exactly, else 10 or (with 2 float4 per lane)
-    // 20, keeping the operand registers of a pass near 160
-    const int T = p.T;
-    const int tc = T <= 8 ? T : (T <= 10 || UP > 2 ? 10 : 20);
+    // tokens per workgroup: up to 8 exactly, else 10 or (with 2 float4 per
+    // lane) 20, keeping the operand registers of a pass near 160
+    const int T = p.T, chunks = router_chunks(p.E, T);
+    const int need = (T + chunks - 1) / chunks;
+    const int tc = need <= 8 ? need : (need <= 10 || UP > 2 ? 10 : 20);
+    const dim3 g(p.E, (T + tc - 1) / tc), b(kRouterThreads);
     switch (tc) {
         case 1: return launch_k(router_kernel<true, 1, UP>, g, b, 0, s, ev, p);
         case 2: return launch_k(router_kernel<true, 2, UP>, g, b, 0, s, ev, p);
@@ -157,7 +166,7 @@ hipError_t launch_router_up(const VerifyParams &p, hipStream_t s, KernelEvents e
 
 hipError_t launch_router(const VerifyParams &p, hipStream_t s, KernelEvents ev) {
     if (p.H % 4 != 0)
-        return launch_k(router_kernel<false, 8, 1>, dim3(p.E), dim3(kRouterThreads), 0, s, ev, p);
+        return launch_k(router_kernel<false, 8, 1>, dim3(p.E, (p.T + 7) / 8), dim3(kRouterThreads), 0, s, ev, p);
     // float4 of the row per wave: 2 per lane cover up to 128
     const int per_wave = (p.H / 4 + kRouterWaves - 1) / kRouterWaves;
     return per_wave <= 128 ? launch_router_up<2>(p, s, ev) : launch_router_up<4>(p, s, ev);
