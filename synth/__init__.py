@@ -445,10 +445,14 @@ def fill_layer_device(wl: Workload, layer: int, device, stream: int = 0) -> dict
     E, H, I = wl.E, wl.H, wl.I
     out = {}
     if wl.wdtype == "bf16":
-        out["W_gu"] = torch.empty((E, 2 * I, H), dtype=torch.int16, device=device)
-        out["W_d"] = torch.empty((E, H, I), dtype=torch.int16, device=device)
-        dev_fill("bf16", out["W_gu"].data_ptr(), E, 2 * I * H, wl.seed, layer, 0, MAT_GU, stream)
-        dev_fill("bf16", out["W_d"].data_ptr(), E, H * I, wl.seed, layer, 0, MAT_D, stream)
+        nE = E + (1 if wl.shared else 0)
+        gu = torch.empty((nE, 2 * I, H), dtype=torch.int16, device=device)
+        d = torch.empty((nE, H, I), dtype=torch.int16, device=device)
+        dev_fill("bf16", gu.data_ptr(), nE, 2 * I * H, wl.seed, layer, 0, MAT_GU, stream)
+        dev_fill("bf16", d.data_ptr(), nE, H * I, wl.seed, layer, 0, MAT_D, stream)
+        out.update(W_gu=gu[:E], W_d=d[:E])
+        if wl.shared:
+            out.update(Wsh_gu=gu[E], Wsh_d=d[E])
     elif wl.wdtype == "fp8":
         nE = E + (1 if wl.shared else 0)
         gu = torch.empty((nE, 2 * I, H), dtype=torch.uint8, device=device)

@@ -175,6 +175,30 @@ def test_fp8_small(T, shared):
     verify_workload(wl)
 
 
+def _random_shape(seed):
+    """Seeded shape within the documented limits: bf16 H % 64, I % 32; fp8
+    H, I % 128; 1 <= k <= min(E, 32), E <= 512, 1 <= T <= 64."""
+    rng = np.random.default_rng(1000 + seed)
+    fp8 = seed % 3 == 2
+    H = int(rng.integers(1, 9)) * (128 if fp8 else 64)
+    I = int(rng.integers(1, 9)) * (128 if fp8 else 32)
+    E = int(rng.choice([8, 16, 40, 96, 200, 512]))
+    k = int(rng.integers(1, min(E, 32) + 1))
+    T = int(rng.integers(1, 65))
+    return fp8, H, I, E, k, T, bool(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    fp8, H, I, E, k, T, shared = _random_shape(seed)
+    log(f"case random seed={seed}: {'fp8' if fp8 else 'bf16'} H={H} I={I} E={E} k={k} T={T} shared={shared}")
+    if fp8:
+        wl = small("deepseek_fp8", H=H, I=I, E=E, k=k, T=T, shared=shared, cid=40 + seed)
+    else:
+        wl = small("qwen3_bf16", H=H, I=I, E=E, k=k, T=T, shared=shared, rate=0.05, cid=40 + seed)
+    verify_workload(wl)
+
+
 def test_fp8_small_with_bias():
     log("case fp8 small with bias T=5")
     wl = small("deepseek_fp8", H=512, I=256, E=32, k=8, T=5, shared=True, cid=11)
