@@ -177,7 +177,8 @@ def test_fp8_small(T, shared):
 
 def _random_shape(seed):
     """Seeded shape within the documented limits: bf16 H % 64, I % 32; fp8
-    H, I % 128; 1 <= k <= min(E, 32), E <= 512, 1 <= T <= 64."""
+    H, I % 128; 1 <= k <= min(E, 32), E <= 512, 1 <= T <= 64; the shared
+    expert and the reuse bias on or off."""
     rng = np.random.default_rng(1000 + seed)
     fp8 = seed % 3 == 2
     H = int(rng.integers(1, 9)) * (128 if fp8 else 64)
@@ -185,18 +186,23 @@ def _random_shape(seed):
     E = int(rng.choice([8, 16, 40, 96, 200, 512]))
     k = int(rng.integers(1, min(E, 32) + 1))
     T = int(rng.integers(1, 65))
-    return fp8, H, I, E, k, T, bool(rng.integers(0, 2))
+    shared = bool(rng.integers(0, 2))
+    bias = None
+    if rng.integers(0, 2):  # reuse bias: k <= cap <= E, 0 <= alpha < 1
+        bias = (int(rng.integers(k, E + 1)), float(rng.random()), rng.random(T).astype(np.float32))
+    return fp8, H, I, E, k, T, shared, bias
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_shapes(seed):
-    fp8, H, I, E, k, T, shared = _random_shape(seed)
-    log(f"case random seed={seed}: {'fp8' if fp8 else 'bf16'} H={H} I={I} E={E} k={k} T={T} shared={shared}")
+    fp8, H, I, E, k, T, shared, bias = _random_shape(seed)
+    log(f"case random seed={seed}: {'fp8' if fp8 else 'bf16'} H={H} I={I} E={E} k={k} T={T} shared={shared} "
+        f"bias={None if bias is None else bias[:2]}")
     if fp8:
         wl = small("deepseek_fp8", H=H, I=I, E=E, k=k, T=T, shared=shared, cid=40 + seed)
     else:
         wl = small("qwen3_bf16", H=H, I=I, E=E, k=k, T=T, shared=shared, rate=0.05, cid=40 + seed)
-    verify_workload(wl)
+    verify_workload(wl, bias_np=bias)
 
 
 def test_fp8_small_with_bias():
