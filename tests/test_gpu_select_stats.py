@@ -95,6 +95,55 @@ def test_expand_odd_shapes():
     assert np.array_equal(S.cpu().numpy(), oexp.expand_batch(trees.parent, trees.P, trees.F, 12.0, 0.4, cd))
 
 
+def _random_trees(seed):
+    """Seeded random trees within the documented limits: BFS parents
+    (parent[i] in [-1, i)), footprints that contain the parent's (a node's
+    own bits OR its parent's), probabilities with ties on odd seeds."""
+    rng = np.random.default_rng(500 + seed)
+    while True:
+        N, W = int(rng.integers(1, 160)), int(rng.integers(1, 64))
+        if N * W + W + 3 * N + N // 32 + 1 <= 16384:
+            break
+    nt = int(rng.integers(1, 48))
+    parent = np.array([-1] + [int(rng.integers(-1, i)) for i in range(1, N)], np.int32)
+    own = (rng.integers(0, 2**32, (nt, N, W), dtype=np.uint64) & rng.integers(0, 2**32, (nt, N, W), dtype=np.uint64)
+           & rng.integers(0, 2**32, (nt, N, W), dtype=np.uint64)).astype(np.uint32)
+    F = own.copy()
+    for i in range(N):
+        if parent[i] >= 0:
+            F[:, i] |= F[:, parent[i]]
+    P = rng.random((nt, N)).astype(np.float32)
+    if seed % 2:
+        P = (np.round(P * 4) / 4).astype(np.float32)
+    return parent, P, F
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_trees(seed):
+    """select_drafts (marginal and static cost) and expand_drafts on random
+    tree shapes, bit for bit against the oracle."""
+    parent, P, F = _random_trees(seed)
+    nt, N, W = F.shape
+    rng = np.random.default_rng(seed)
+    gamma = int(rng.integers(0, N + 1))
+    log(f"case random trees seed={seed}: nt={nt} N={N} W={W} gamma={gamma}")
+    Pd, Fd = to_dev(P), to_dev(F.view(np.int32))
+    for static in (False, True):
+        S = m.select_drafts(parent, Pd, Fd, gamma, static=static)
+        torch.cuda.synchronize()
+        assert np.array_equal(S.cpu().numpy(), osel.select_drafts_batch(P, F, gamma, static=static)), static
+    # the expert cost is scaled to the footprint density (about 4 W own bits
+    # per node) so that some expansions grow and some stop
+    cd = rng.uniform(0, 2, P.shape).astype(np.float32)
+    t_ar = float(rng.uniform(1, 40))
+    t_exp = float(t_ar * rng.uniform(0, 0.5) / (4 * W))
+    S, cnt = m.expand_drafts(parent, Pd, Fd, t_ar, t_exp, to_dev(cd))
+    torch.cuda.synchronize()
+    ref = oexp.expand_batch(parent, P, F, t_ar, t_exp, cd)
+    assert np.array_equal(S.cpu().numpy(), ref)
+    assert np.array_equal(cnt.cpu().numpy(), (ref >= 0).sum(axis=1))
+
+
 def chains(seed, S, Dmax, n_layers, E, k):
     """S sequences of Dmax chained drafts: cumulative confidences and the
     expert bitsets of each sequence's root and drafts."""
