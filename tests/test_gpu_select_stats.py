@@ -179,6 +179,39 @@ def test_union_stats_segments():
     assert np.array_equal(per.cpu().numpy(), rp) and np.array_equal(tot.cpu().numpy(), rt)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_ragged(seed):
+    """union_stats_segments on random segmentations (empty segments, entries
+    outside [0, E) that must be ignored) and gate_depths on random chains
+    and costs, bit for bit against the oracle."""
+    rng = np.random.default_rng(700 + seed)
+    S = int(rng.integers(1, 65))
+    sizes = rng.integers(0, 3, S)
+    sizes[rng.integers(0, S)] += 1                     # at least one token
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = int(off[-1])
+    E = int(rng.choice([8, 37, 128, 300, 512]))
+    k = int(rng.integers(1, min(E, 32) + 1))
+    nL = int(rng.integers(1, 20))
+    idx = np.stack([np.stack([rng.choice(E, k, replace=False) for _ in range(T)]) for _ in range(nL)]).astype(np.int32)
+    bad = rng.random(idx.shape) < 0.02
+    idx[bad] = rng.choice([-1, E, E + 7], int(bad.sum()))
+    log(f"case random ragged seed={seed}: S={S} T={T} E={E} k={k} nL={nL}")
+    per, tot = m.union_stats_segments(to_dev(idx), E, off)
+    torch.cuda.synchronize()
+    rp, rt = orag.segment_union_stats(idx, off, E)
+    assert np.array_equal(per.cpu().numpy(), rp) and np.array_equal(tot.cpu().numpy(), rt)
+    # depth gating: S2 sequences, random depth bound, costs around the break-even
+    S2, Dmax = int(rng.integers(1, 65)), int(rng.integers(0, 13))
+    c, Ep = chains(800 + seed, S2, Dmax, 36, 128, 4) if Dmax > 0 else (np.ones((S2, 1), np.float32), None)
+    if Ep is None:
+        Ep = chains(800 + seed, S2, 1, 36, 128, 4)[1][:, :1]
+    t_base, t_exp = float(rng.uniform(10, 1000)), float(rng.uniform(0, 2))
+    d = m.gate_depths(to_dev(c), to_dev(np.ascontiguousarray(Ep).view(np.int32)), t_base, t_exp)
+    torch.cuda.synchronize()
+    assert d.cpu().numpy().tolist() == orag.gate_depths(c, Ep, t_base, t_exp)
+
+
 @pytest.mark.parametrize("E,T,k", [(128, 5, 8), (128, 20, 8), (300, 7, 3), (8, 4, 2)])
 def test_union_stats(E, T, k):
     log(f"case union_stats E={E} T={T} k={k}")
