@@ -107,6 +107,39 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+# torch dtype names accepted for each weight format (bf16 weights may be given
+# as bf16 or as their 16-bit patterns; fp8 as float8_e4m3fn or as uint8 codes)
+_WDT = {"f32": ("float32",), "bf16": ("bfloat16", "int16", "uint16"), "fp8": ("uint8", "float8_e4m3fn")}
+
+
+def _dtname(t) -> str:
+    return str(t.dtype).replace("torch.", "")
+
+
+def _check_tensor(t, name: str, dtypes, numel: Optional[int] = None, shape=None, device=None,
+                  at_least: bool = False) -> None:
+    """Raise ValueError unless t is a contiguous tensor with one of `dtypes`,
+    the given shape (or element count; `at_least`: no fewer elements) and on
+    `device`.  The C ABI sees only pointers, so these checks are what keeps
+    the kernels inside the caller's buffers."""
+    if t is None:
+        raise ValueError(f"{name} is missing")
+    if not hasattr(t, "data_ptr") or not hasattr(t, "is_contiguous"):
+        raise ValueError(f"{name} must be a tensor")
+    if _dtname(t) not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(dtypes)}, got {_dtname(t)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None:
+        n = t.numel()
+        if (n < numel) if at_least else (n != numel):
+            raise ValueError(f"{name} must have {'at least ' if at_least else ''}{numel} elements, got {n}")
+
+
 @dataclass
 class LayerWeights:
     """Device tensors of one MoE layer (layouts in include/moe_verify.h).
@@ -128,6 +161,49 @@ class LayerWeights:
     Wsh_d: object = None
     ssh_gu: object = None
     ssh_d: object = None
+
+    def __setattr__(self, name, value):
+        # any reassignment invalidates the result of the last validate()
+        object.__setattr__(self, "_valid_on", None)
+        object.__setattr__(self, name, value)
+
+    def validate(self, device) -> None:
+        """Check every tensor against the layout of include/moe_verify.h
+        (dtype, element count, contiguity, device); raises ValueError.  The
+        result is remembered until a field is reassigned (tensors resized in
+        place are not noticed)."""
+        if getattr(self, "_valid_on", None) == device:
+            return
+        self._check_fields(device)
+        object.__setattr__(self, "_valid_on", device)
+
+    def _check_fields(self, device) -> None:
+        H, I, E, k, wd = self.H, self.I, self.E, self.k, self.wdtype
+        if wd not in DTYPES:
+            raise ValueError(f"unknown wdtype {wd!r}")
+        if min(H, I, E, k) < 1:
+            raise ValueError("H, I, E and k must be positive")
+        _check_tensor(self.Wr, "Wr", ("float32",), numel=E * H, device=device)
+        _check_tensor(self.W_gu, "W_gu", _WDT[wd], numel=E * 2 * I * H, device=device)
+        _check_tensor(self.W_d, "W_d", _WDT[wd], numel=E * H * I, device=device)
+        if (self.Wsh_gu is None) != (self.Wsh_d is None):
+            raise ValueError("the shared expert needs both Wsh_gu and Wsh_d")
+        if self.Wsh_gu is not None:
+            _check_tensor(self.Wsh_gu, "Wsh_gu", _WDT[wd], numel=2 * I * H, device=device)
+            _check_tensor(self.Wsh_d, "Wsh_d", _WDT[wd], numel=H * I, device=device)
+        if wd == "fp8":
+            if H % 128 or I % 128:
+                raise ValueError("fp8 weights need H and I multiples of 128")
+            gs, ds = (2 * I // 128) * (H // 128), (H // 128) * (I // 128)
+            _check_tensor(self.s_gu, "s_gu", ("float32",), numel=E * gs, device=device)
+            _check_tensor(self.s_d, "s_d", ("float32",), numel=E * ds, device=device)
+            if self.Wsh_gu is not None:
+                _check_tensor(self.ssh_gu, "ssh_gu", ("float32",), numel=gs, device=device)
+                _check_tensor(self.ssh_d, "ssh_d", ("float32",), numel=ds, device=device)
+        else:
+            for name in ("s_gu", "s_d", "ssh_gu", "ssh_d"):
+                if getattr(self, name) is not None:
+                    raise ValueError(f"{name} is only used with fp8 weights")
 
     def _c(self) -> _Layer:
         return _Layer(self.H, self.I, self.E, self.k, DTYPES[self.wdtype], _ptr(self.Wr), _ptr(self.W_gu),
@@ -227,6 +303,10 @@ def expert_bytes(H: int, I: int, wdtype: str) -> int:
 
 @dataclass
 class Aux:
+    def __setattr__(self, name, value):
+        object.__setattr__(self, "_valid", False)
+        object.__setattr__(self, name, value)
+
     logits: object
     topk_idx: object
     topk_w: object
@@ -246,6 +326,10 @@ class Workspace:
     nbytes: int
     aux: Optional[Aux] = None
     extra: dict = field(default_factory=dict)
+
+    def __setattr__(self, name, value):
+        object.__setattr__(self, "_valid_for", None)
+        object.__setattr__(self, name, value)
 
 
 def alloc_aux(layer: LayerWeights, T: int, device) -> Aux:
@@ -275,6 +359,36 @@ def alloc_workspace(layer: LayerWeights, T: int, bias: Optional[Bias] = None, de
     return Workspace(ws=ws, nbytes=n, aux=alloc_aux(layer, T, device) if with_aux else None)
 
 
+def _aux_sizes(layer: LayerWeights, T: int):
+    """Element count and dtype of each Aux field (include/moe_verify.h)."""
+    E, k = layer.E, layer.k
+    i32, f32 = ("int32",), ("float32",)
+    return {"logits": (T * E, f32), "topk_idx": (T * k, i32), "topk_w": (T * k, f32), "union_size": (1, i32),
+            "union_experts": (E, i32), "csr_ptr": (E + 1, i32), "csr_tok": (T * k, i32), "csr_w": (T * k, f32),
+            "pstar": (E, i32), "pstar_size": (1, i32)}
+
+
+def _check_workspace(wsp: Workspace, layer: LayerWeights, T: int, bias: Optional[Bias], dev) -> None:
+    """A caller-supplied workspace must hold at least what this call needs:
+    the C side trusts the byte count it is given.  The last passing
+    (layer shape, T, bias cap, device) is remembered until a field of the
+    workspace or of its aux is reassigned."""
+    key = (layer.H, layer.I, layer.E, layer.k, layer.wdtype, T, None if bias is None else bias.cap, dev)
+    if getattr(wsp, "_valid_for", None) == key and (wsp.aux is None or getattr(wsp.aux, "_valid", False)):
+        return
+    need = workspace_bytes(layer, T, bias)
+    if wsp.nbytes < need:
+        raise ValueError(f"workspace holds {wsp.nbytes} bytes, this call needs {need}")
+    _check_tensor(wsp.ws, "workspace.ws", ("uint8", "int8"), numel=wsp.nbytes, device=dev, at_least=True)
+    if wsp.aux is not None:
+        for f, (n, dt) in _aux_sizes(layer, T).items():
+            t = getattr(wsp.aux, f)
+            if t is not None:
+                _check_tensor(t, f"workspace.aux.{f}", dt, numel=n, device=dev, at_least=True)
+        object.__setattr__(wsp.aux, "_valid", True)
+    object.__setattr__(wsp, "_valid_for", key)
+
+
 def verify_layer(x, layer: LayerWeights, bias: Optional[Bias] = None, *, out=None,
                  workspace: Optional[Workspace] = None, events: Optional[Sequence] = None, stream=None):
     """One MoE-layer verify step for x [T, H] float32 (device).  Returns
@@ -284,15 +398,26 @@ def verify_layer(x, layer: LayerWeights, bias: Optional[Bias] = None, *, out=Non
     another stream the launch first waits for the current stream, and the
     buffers are marked as used by the launch stream."""
     import torch
-    T = int(x.shape[0])
-    if x.dtype != torch.float32 or x.dim() != 2 or x.shape[1] != layer.H or not x.is_contiguous():
+    if not hasattr(x, "dim") or x.dim() != 2:
         raise ValueError("x must be a contiguous float32 [T, H] tensor")
+    T = int(x.shape[0])
+    dev = x.device
+    _check_tensor(x, "x", ("float32",), shape=(T, layer.H))
+    if dev.type != "cuda":
+        raise ValueError(f"x must be a device tensor, got {dev}")
+    layer.validate(dev)
+    if bias is not None:
+        _check_tensor(bias.w_conf, "bias.w_conf", ("float32",), numel=T, device=dev)
     owned = []
     if workspace is None:
-        workspace = alloc_workspace(layer, T, bias, device=x.device)
+        workspace = alloc_workspace(layer, T, bias, device=dev)
         owned.append(workspace.ws)
         if workspace.aux is not None:
             owned += [getattr(workspace.aux, f) for f in Aux.__dataclass_fields__]
+    else:
+        _check_workspace(workspace, layer, T, bias, dev)
+    if out is not None:
+        _check_tensor(out, "out", ("float32",), shape=(T, layer.H), device=dev)
     y = out if out is not None else torch.empty_like(x)
     if out is None:
         owned.append(y)
@@ -324,9 +449,13 @@ def union_stats(topk_idx, E: int, counts=None, reuse=None, stream=None):
     if counts is None:
         counts = torch.empty(nL, dtype=torch.int32, device=topk_idx.device)
         owned.append(counts)
+    else:
+        _check_tensor(counts, "counts", ("int32",), shape=(nL,), device=topk_idx.device)
     if reuse is None:
         reuse = torch.empty(nL, dtype=torch.float32, device=topk_idx.device)
         owned.append(reuse)
+    else:
+        _check_tensor(reuse, "reuse", ("float32",), shape=(nL,), device=topk_idx.device)
     s = _launch_stream(stream, topk_idx.device, owned)
     _check(lib().union_stats(topk_idx.data_ptr(), nL, T, k, E, counts.data_ptr(), reuse.data_ptr(), s))
     return counts, reuse
@@ -347,6 +476,10 @@ def select_drafts(parent, P, Epred, gamma: int, eps: float = 1e-6, out=None, str
     if tuple(Epred.shape[:2]) != (nt, N) or par.shape != (N,):
         raise ValueError("shape mismatch between parent, P and Epred")
     W = int(Epred.shape[2])
+    if Epred.device != P.device:
+        raise ValueError("P and Epred must be on the same device")
+    if out is not None:
+        _check_tensor(out, "out", ("int32",), shape=(nt, gamma), device=P.device)
     S = out if out is not None else torch.empty((nt, gamma), dtype=torch.int32, device=P.device)
     s = _launch_stream(stream, P.device, [S] if out is None else [])
     fn = lib().select_drafts_static if static else lib().select_drafts
@@ -371,6 +504,8 @@ def expand_drafts(parent, P, Epred, t_ar: float, t_exp: float, c_draft=None, str
     if c_draft is not None and (c_draft.dtype != torch.float32 or tuple(c_draft.shape) != (nt, N)
                                 or not c_draft.is_contiguous()):
         raise ValueError("c_draft must be a contiguous float32 [nt, N] tensor")
+    if Epred.device != P.device or (c_draft is not None and c_draft.device != P.device):
+        raise ValueError("P, Epred and c_draft must be on the same device")
     W = int(Epred.shape[2])
     S = torch.empty((nt, N), dtype=torch.int32, device=P.device)
     count = torch.empty((nt,), dtype=torch.int32, device=P.device)
@@ -411,6 +546,8 @@ def gate_depths(c, Epred, t_base: float, t_exp: float, stream=None):
     S, D1 = (int(v) for v in c.shape)
     if tuple(Epred.shape[:2]) != (S, D1):
         raise ValueError("shape mismatch between c and Epred")
+    if Epred.device != c.device:
+        raise ValueError("c and Epred must be on the same device")
     d = torch.empty((S,), dtype=torch.int32, device=c.device)
     s = _launch_stream(stream, c.device, [d])
     _check(lib().gate_depths(c.data_ptr(), Epred.data_ptr(), S, D1 - 1, int(Epred.shape[2]), t_base, t_exp,

@@ -130,8 +130,13 @@ constexpr int kRouteThreads = 512;  // one thread per expert at the most experts
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(VerifyParams p) {
     extern __shared__ __align__(16) unsigned char dyn[];
     __shared__ int nslots;
-    // the slot tables go straight to the workspace
-    block_route<kRouteThreads>(p, dyn, p.slot_expert, p.tokw, &nslots, true);
+    // The expert of each slot is written by wave 0 and read back by the other
+    // waves after an LDS-only barrier, so it must live in LDS; the routing
+    // writes the workspace copy (slot_expert) itself.  The gate weights per
+    // (slot, token) are only written, each by one thread, and go straight to
+    // the workspace.
+    __shared__ int sexp[kMaxExperts + 1];
+    block_route<kRouteThreads>(p, dyn, sexp, p.tokw, &nslots, true);
 }
 
 // Token chunks per expert: enough workgroups for the 256 compute units.

@@ -218,14 +218,20 @@ def csr(topk_idx: np.ndarray, topk_w: np.ndarray) -> CSR:
                w=np.array(w, dtype=np.float64))
 
 
-def union_stats(topk_idx_layers: np.ndarray):
+def union_stats(topk_idx_layers: np.ndarray, E: Optional[int] = None):
     """Per layer: number of unique experts and reuse ratio |U| / (T k).
 
     Counts are integers; the ratio is the correctly rounded float32 quotient
-    of two small integers ([S2-MoE] motivation, challenge 2)."""
+    of two small integers ([S2-MoE] motivation, challenge 2).  With ``E``
+    given, entries outside [0, E) name no expert and are left out of the
+    union (the denominator stays T k: it counts the routing slots)."""
     a = np.asarray(topk_idx_layers)
     nL, T, k = a.shape
-    counts = np.array([len(expert_union(a[l])) for l in range(nL)], dtype=np.int32)
+
+    counts = np.zeros(nL, dtype=np.int32)
+    for l in range(nL):
+        named = [int(e) for e in a[l].ravel() if E is None or 0 <= e < E]
+        counts[l] = len(set(named))
     reuse = np.array([np.float32(c) / np.float32(T * k) for c in counts], dtype=np.float32)
     return counts, reuse
 

@@ -16,7 +16,7 @@ from oracle import moe as omoe
 # Output tolerances, max |y - y_oracle| <= TOL * RMS(y_oracle), by weight format.
 TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 5e-2}
 # Tighter bound when activations enter the products as a bf16 high/low pair
-# (T <= 32): weights are exact, activations carry ~2^-16 relative error, and
+# (2T <= 16, i.e. T <= 8): weights are exact, activations carry ~2^-16 relative error, and
 # accumulation is float32, so errors stay orders of magnitude below 1e-3.
 TOL_SPLIT = 1e-3
 

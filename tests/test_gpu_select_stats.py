@@ -220,12 +220,18 @@ def test_union_stats(E, T, k):
     L = np.stack([synth.structured_logits(rng, 1, T, E, 0.05) for _ in range(nL)]).astype(np.float32)
     idx = np.stack([omoe.topk(L[l], k) for l in range(nL)])
     idx[0] = idx[0][:1]                          # identical tokens: union == k
+    # entries outside [0, E) name no expert and are ignored (layers 1 and 2)
+    idx[1, 0, 0] = -1
+    idx[1, T - 1, k - 1] = E
+    idx[2, :, :] = E + 7
+    idx[2, 0, 0] = 0
     counts, reuse = m.union_stats(to_dev(idx), E)
     torch.cuda.synchronize()
-    rc, rr = omoe.union_stats(idx)
+    rc, rr = omoe.union_stats(idx, E)
     assert np.array_equal(counts.cpu().numpy(), rc)
     assert np.array_equal(reuse.cpu().numpy(), rr)
     assert counts[0].item() == k
+    assert counts[2].item() == 1
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8", "scale"])

@@ -164,6 +164,27 @@ def test_union_stats_counts_and_exact_ratio():
         assert reuse[l] == np.float32(counts[l] / 20)
 
 
+def test_union_stats_ignores_entries_outside_the_experts():
+    # one rule for both statistics calls: an entry outside [0, E) names no
+    # expert, so it adds nothing to the union; T k stays the denominator
+    E = 16
+    a = np.array([[[3, -1], [3, 16], [5, 99]],          # {3, 5}
+                  [[-7, -7], [16, 17], [40, 16]],       # nothing in range
+                  [[0, 15], [15, 0], [1, 2]]], dtype=np.int32)  # {0, 1, 2, 15}
+    counts, reuse = moe.union_stats(a, E)
+    assert counts.tolist() == [2, 0, 4]
+    assert reuse.tolist() == [np.float32(2 / 6), 0.0, np.float32(4 / 6)]
+    # brute force on random rows with a third of the entries out of range
+    rng = np.random.default_rng(31)
+    b = rng.integers(-20, 2 * E, size=(40, 7, 3)).astype(np.int32)
+    c2, _ = moe.union_stats(b, E)
+    for l in range(40):
+        assert c2[l] == len({int(e) for e in b[l].ravel() if 0 <= e < E})
+    # without E every entry counts (the verify layer's own selections are in range)
+    c3, _ = moe.union_stats(a)
+    assert c3.tolist() == [5, 4, 4]
+
+
 # ---------------------------------------------------------------------------
 # Expert FFN and layer output
 # ---------------------------------------------------------------------------

@@ -81,3 +81,14 @@ def test_segment_union_stats():
         c1, _ = omoe.union_stats(idx[:, off[s]:off[s + 1]])
         assert np.array_equal(per[:, s], c1)
     assert (per.max(axis=1) <= tot).all() and (tot <= per.sum(axis=1)).all()
+
+
+def test_segment_union_stats_ignores_out_of_range_and_empty_segments():
+    E = 10
+    idx = np.array([[[1, 2], [2, -1], [10, 3], [9, 0]]], dtype=np.int32)   # one layer, T = 4, k = 2
+    off = np.array([0, 2, 2, 4])                                              # segment 1 is empty
+    per, tot = ragged.segment_union_stats(idx, off, E)
+    assert per.tolist() == [[2, 0, 3]]        # {1, 2}; {}; {3, 9, 0}
+    assert tot.tolist() == [5]                # {0, 1, 2, 3, 9}
+    counts, _ = omoe.union_stats(idx, E)
+    assert tot.tolist() == counts.tolist()
