@@ -35,7 +35,13 @@ documented choice; tests pin them):
       the original logits over the new selection.
   R13 the always-on shared expert has weight 1, is outside the union and
       outside the union statistics.
-  R16 bias aggregation runs over all tokens of the call.
+  R16 bias aggregation runs over all tokens of the call, unless the call's
+      tokens are grouped by sequence (segment offsets, as in a ragged or
+      batched verify call): then the importance and the preferred set are
+      those of each sequence's own tokens, and a token is biased toward its
+      own sequence's preferred set (each sequence verifies its own drafts;
+      [W-vs-D] section 2, ragged speculation; [S2-MoE] component 2, steps
+      1-2, whose candidate set is one sequence's drafts).
   R20 expert FFN = SwiGLU: W_d (SiLU(W_g x) * (W_u x)), SiLU(z) = z / (1 + e^-z).
 """
 from __future__ import annotations
@@ -173,6 +179,57 @@ def reuse_bias(logits32: np.ndarray, w_conf: np.ndarray, k: int, cap: int, alpha
     return BiasResult(g=g, pstar=ps, lam=lam, biased=biased, topk_idx=idx1, topk_w=w1)
 
 
+@dataclass
+class SegmentBiasResult:
+    offsets: np.ndarray      # [S + 1] token offsets of the sequences
+    g: np.ndarray            # [S, E] float64 importance of each sequence's tokens (R4, R16)
+    pstar: list              # S arrays, each sequence's preferred set (R5)
+    lam: np.ndarray          # [T] float32 per-token bias size (R6)
+    biased: np.ndarray       # [T, E] float32 biased logits (R6)
+    topk_idx: np.ndarray     # [T, k] int32
+    topk_w: np.ndarray       # [T, k] float64 (R7)
+
+
+def check_offsets(offsets, T: int) -> np.ndarray:
+    off = np.asarray(offsets, dtype=np.int64)
+    if off.ndim != 1 or len(off) < 2 or off[0] != 0 or off[-1] != T or np.any(np.diff(off) < 0):
+        raise ValueError("offsets must be non-decreasing from 0 to T")
+    return off
+
+
+def reuse_bias_segments(logits32: np.ndarray, w_conf: np.ndarray, k: int, cap: int, alpha: float,
+                        offsets, pstar=None) -> SegmentBiasResult:
+    """Reuse-aware soft bias with the tokens grouped by sequence (R16): the
+    pooled bias of ``reuse_bias`` applied to each sequence's rows
+    offsets[s] .. offsets[s+1]-1 on their own.  ``pstar`` (optional) gives
+    each sequence's preferred set instead of the computed one."""
+    l = np.asarray(logits32, dtype=np.float32)
+    T, E = l.shape
+    off = check_offsets(offsets, T)
+    S = len(off) - 1
+    if not (k <= cap <= E):
+        raise ValueError("need k <= cap <= E")
+    if not (0.0 <= alpha < 1.0):
+        raise ValueError("need 0 <= alpha < 1")
+    g = np.zeros((S, E), dtype=np.float64)
+    ps = []
+    lam = np.zeros(T, dtype=np.float32)
+    biased = l.copy()
+    idx = np.zeros((T, k), dtype=np.int32)
+    w = np.zeros((T, k), dtype=np.float64)
+    for s in range(S):
+        a, b = int(off[s]), int(off[s + 1])
+        if a == b:
+            ps.append(np.zeros(0, dtype=np.int32))
+            continue
+        r = reuse_bias(l[a:b], np.asarray(w_conf)[a:b], k, cap, alpha,
+                       pstar=None if pstar is None else pstar[s])
+        g[s], lam[a:b], biased[a:b], idx[a:b], w[a:b] = r.g, r.lam, r.biased, r.topk_idx, r.topk_w
+        ps.append(r.pstar)
+    return SegmentBiasResult(offsets=off.astype(np.int32), g=g, pstar=ps, lam=lam, biased=biased,
+                             topk_idx=idx, topk_w=w)
+
+
 # ----------------------------------------------------------------------------
 # Union and grouping
 # ----------------------------------------------------------------------------
@@ -281,12 +338,17 @@ class Routing:
 
 
 def route(logits32: np.ndarray, k: int, w_conf: Optional[np.ndarray] = None, cap: int = 0,
-          alpha: float = 0.0, pstar: Optional[np.ndarray] = None) -> Routing:
+          alpha: float = 0.0, pstar=None, offsets=None) -> Routing:
     """Routing of one call: top-k and gate weights, with the optional reuse
-    bias when ``w_conf`` is given."""
+    bias when ``w_conf`` is given, pooled over the call or, with sequence
+    ``offsets``, per sequence (then ``pstar`` is a list, one set per
+    sequence)."""
     l = np.asarray(logits32, dtype=np.float32)
     if w_conf is None:
         idx = topk(l, k)
         return Routing(l, idx, gate_weights(l, idx), None)
-    b = reuse_bias(l, w_conf, k, cap, alpha, pstar=pstar)
+    if offsets is not None:
+        b = reuse_bias_segments(l, w_conf, k, cap, alpha, offsets, pstar=pstar)
+    else:
+        b = reuse_bias(l, w_conf, k, cap, alpha, pstar=pstar)
     return Routing(l, b.topk_idx, b.topk_w, b)

@@ -341,6 +341,99 @@ def test_bias_float32_steps_by_hand():
 
 
 # ---------------------------------------------------------------------------
+# Reuse bias with the tokens grouped by sequence (R16)
+# ---------------------------------------------------------------------------
+def _random_offsets(rng, T):
+    S = int(rng.integers(1, 6))
+    cuts = np.sort(rng.integers(0, T + 1, size=S - 1))
+    return np.concatenate([[0], cuts, [T]]).astype(np.int32)     # may hold empty sequences
+
+
+def test_segments_one_sequence_is_the_pooled_bias():
+    rng = np.random.default_rng(40)
+    for _ in range(100):
+        L, w, k, cap, alpha = _random_bias_case(rng)
+        T = L.shape[0]
+        b = moe.reuse_bias(L, w, k, cap, alpha)
+        sb = moe.reuse_bias_segments(L, w, k, cap, alpha, [0, T])
+        assert np.array_equal(sb.topk_idx, b.topk_idx) and np.array_equal(sb.topk_w, b.topk_w)
+        assert np.array_equal(sb.pstar[0], b.pstar) and np.array_equal(sb.biased, b.biased)
+
+
+def test_segments_each_sequence_union_never_grows():
+    # the bias only moves a token onto experts that its own sequence's
+    # tokens already chose, so no sequence's expert set grows, and neither
+    # does the call's
+    rng = np.random.default_rng(41)
+    for _ in range(300):
+        L, w, k, cap, alpha = _random_bias_case(rng)
+        T = L.shape[0]
+        off = _random_offsets(rng, T)
+        sb = moe.reuse_bias_segments(L, w, k, cap, alpha, off)
+        idx0 = moe.topk(L, k)
+        for s in range(len(off) - 1):
+            a, b = off[s], off[s + 1]
+            U0 = {int(e) for e in idx0[a:b].ravel()}
+            assert {int(e) for e in sb.topk_idx[a:b].ravel()} <= U0
+            assert set(sb.pstar[s].tolist()) <= U0 and len(sb.pstar[s]) <= cap
+            if a == b:
+                assert len(sb.pstar[s]) == 0
+        assert set(moe.expert_union(sb.topk_idx).tolist()) <= set(moe.expert_union(idx0).tolist())
+        top1 = idx0[:, 0]
+        assert all(top1[t] in sb.topk_idx[t] for t in range(T))
+
+
+def test_segments_fig5_inside_one_sequence_and_independence():
+    g = load("fig5_reuse_gating.json")
+    facts = g["page_facts"]
+    fig = np.array(g["logits"], dtype=np.float32)
+    rng = np.random.default_rng(42)
+    before = rng.standard_normal((3, 8)).astype(np.float32)
+    after = rng.standard_normal((2, 8)).astype(np.float32)
+    L = np.concatenate([before, fig, after])
+    w = np.concatenate([rng.random(3), np.array(g["w_conf"]), rng.random(2)])
+    off = [0, 3, 7, 9]
+    sb = moe.reuse_bias_segments(L, w, facts["k"], g["cap"], g["alpha"], off)
+    mid = sb.topk_idx[3:7]
+    assert len(moe.expert_union(moe.topk(fig, facts["k"]))) == facts["unique_experts_without_bias"]
+    assert len(moe.expert_union(mid)) == facts["unique_experts_with_bias"]
+    assert sorted(sb.pstar[1].tolist()) == facts["preferred_set_zero_based"]
+    # the other sequences' tokens and confidences do not reach this one
+    L2 = L.copy()
+    L2[:3] = rng.standard_normal((3, 8)).astype(np.float32) * 3
+    L2[7:] = -L2[7:]
+    w2 = w.copy()
+    w2[[0, 8]] = [5.0, 0.0]
+    sb2 = moe.reuse_bias_segments(L2, w2, facts["k"], g["cap"], g["alpha"], off)
+    assert np.array_equal(sb2.topk_idx[3:7], mid) and np.array_equal(sb2.topk_w[3:7], sb.topk_w[3:7])
+
+
+def test_pooled_bias_crosses_sequences_and_per_sequence_does_not():
+    # sequence A: one token on {0, 1}; sequence B: two confident tokens on
+    # {2, 3}.  Pooled, P* = {2, 3} pulls A's token onto expert 2, which only
+    # B uses; per sequence, A's preferred set is its own {0, 1}.
+    L = np.zeros((3, 8), dtype=np.float32)
+    L[0, :3] = [3.0, 2.0, 1.9]
+    L[1, 2:4] = [5.0, 4.9]
+    L[2, 2:4] = [5.0, 4.8]
+    w = np.array([0.1, 1.0, 1.0])
+    pooled = moe.reuse_bias(L, w, 2, 2, 0.9)
+    per = moe.reuse_bias_segments(L, w, 2, 2, 0.9, [0, 1, 3])
+    assert sorted(pooled.pstar.tolist()) == [2, 3]
+    assert sorted(pooled.topk_idx[0].tolist()) == [0, 2]
+    assert sorted(per.pstar[0].tolist()) == [0, 1] and sorted(per.pstar[1].tolist()) == [2, 3]
+    assert sorted(per.topk_idx[0].tolist()) == [0, 1]
+    assert len(moe.expert_union(pooled.topk_idx)) == 3 and len(moe.expert_union(per.topk_idx)) == 4
+
+
+def test_segment_offsets_validated():
+    L = np.zeros((4, 6), dtype=np.float32)
+    for bad in ([0, 5], [1, 4], [0, 3, 2, 4], [0]):
+        with pytest.raises(ValueError):
+            moe.reuse_bias_segments(L, np.ones(4), 2, 3, 0.5, bad)
+
+
+# ---------------------------------------------------------------------------
 # Number formats
 # ---------------------------------------------------------------------------
 def test_e4m3fn_spec_values():
