@@ -46,6 +46,7 @@ extern "C" {
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 32
 #define MOE_NUM_STAGES 5   /* router, route, gate-up, down, combine */
+#define MOE_MAX_SEGMENTS 64 /* sequences of one call with a preferred set of their own */
 
 /* Expert weight formats.  MOE_FP8_E4M3 is OCP FP8 E4M3FN with one float32
  * scale per 128 x 128 block (row block, column block), row-major over blocks:
@@ -85,11 +86,22 @@ typedef struct {
  *   l'_b,e = l_b,e + lambda_b for e in P*           (float32)
  * The selection is the top-k of l'; gate weights are the softmax of the
  * ORIGINAL logits over that selection.  Requires k <= cap <= E,
- * 0 <= alpha < 1, w_conf [T] float32 (device) non-negative. */
+ * 0 <= alpha < 1, w_conf [T] float32 (device) non-negative.
+ * Sequences ([W-vs-D] section 2, ragged speculation: one call verifies the
+ * drafts of several sequences): with nseg = 0 the sums run over all T tokens
+ * of the call (one P*); with nseg > 0 the tokens are grouped by sequence,
+ * rows seg_off[s] .. seg_off[s+1]-1 forming sequence s, and g and P* are
+ * computed over each sequence's own tokens, each token biased toward its own
+ * sequence's P* (so no token is pushed toward experts that only other
+ * sequences chose).  seg_off (host) [nseg + 1], 0 = seg_off[0] <= ... <=
+ * seg_off[nseg] = T (empty sequences allowed), read during the call only;
+ * nseg <= MOE_MAX_SEGMENTS.  Errors: EINVAL. */
 typedef struct {
     int32_t cap;
     float alpha;
     const float *w_conf;
+    int32_t nseg;
+    const int32_t *seg_off;
 } moe_bias;
 
 /* Optional outputs of moe_verify_layer (device pointers); any field may be
@@ -103,7 +115,10 @@ typedef struct {
  *   csr_ptr [E + 1] i32        first U + 1 entries: offsets into csr_tok
  *   csr_tok [T * k] i32        tokens of each union expert, ascending
  *   csr_w [T * k] f32          gate weight of each (expert, token) entry
- *   pstar [E] i32, pstar_size [1] i32   preferred set P* (bias only)
+ *   pstar [S, cap] i32, pstar_size [S] i32   preferred set of each sequence
+ *                              (S = max(1, nseg); row s holds sequence s's P*
+ *                              ascending in its first pstar_size[s] entries;
+ *                              bias only; without the bias pstar_size[0] = 0)
  *   events: NULL or (host) array of 2 * MOE_NUM_STAGES hipEvent_t handles
  *           created by the caller with timing enabled.  Events 2i and 2i + 1
  *           mark the start and the end of the execution of stage i's kernel

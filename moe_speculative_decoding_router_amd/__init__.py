@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libmoeverify.so")
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 NUM_STAGES = 5
+MAX_SEGMENTS = 64
 STAGE_NAMES = ("router", "route", "gate_up", "down", "combine")
 EXPORTED = ("moe_pack_weights", "moe_verify_workspace_bytes", "moe_verify_layer", "union_stats",
             "select_drafts", "select_drafts_static", "expand_drafts", "union_stats_segments", "gate_depths",
@@ -45,7 +46,7 @@ class _Layer(ctypes.Structure):
 
 
 class _Bias(ctypes.Structure):
-    _fields_ = [("cap", _i32), ("alpha", _f32), ("w_conf", _vp)]
+    _fields_ = [("cap", _i32), ("alpha", _f32), ("w_conf", _vp), ("nseg", _i32), ("seg_off", _vp)]
 
 
 class _Aux(ctypes.Structure):
@@ -213,13 +214,35 @@ class LayerWeights:
 
 @dataclass
 class Bias:
-    """Reuse-aware soft bias parameters (w_conf: [T] float32 device tensor)."""
+    """Reuse-aware soft bias parameters (w_conf: [T] float32 device tensor).
+    offsets: None (the importance and the preferred set are pooled over the
+    call) or the [S + 1] token offsets of the call's sequences, each with its
+    own preferred set (host sequence of ints, 0 .. T)."""
     cap: int
     alpha: float
     w_conf: object
+    offsets: Optional[Sequence[int]] = None
+
+    @property
+    def nseq(self) -> int:
+        """Sequences with a preferred set of their own (1 when pooled)."""
+        return 1 if self.offsets is None else len(self.offsets) - 1
+
+    def check(self, T: int, device) -> None:
+        _check_tensor(self.w_conf, "bias.w_conf", ("float32",), numel=T, device=device)
+        if self.offsets is not None:
+            off = np.asarray(self.offsets)
+            if (off.ndim != 1 or len(off) < 2 or len(off) - 1 > MAX_SEGMENTS or off[0] != 0 or off[-1] != T
+                    or np.any(np.diff(off) < 0)):
+                raise ValueError(f"bias.offsets must be 2 .. {MAX_SEGMENTS + 1} non-decreasing offsets from 0 to T={T}")
 
     def _c(self) -> _Bias:
-        return _Bias(self.cap, self.alpha, _ptr(self.w_conf))
+        if self.offsets is None:
+            return _Bias(self.cap, self.alpha, _ptr(self.w_conf), 0, None)
+        off = np.ascontiguousarray(np.asarray(self.offsets, dtype=np.int32))
+        c = _Bias(self.cap, self.alpha, _ptr(self.w_conf), len(off) - 1, off.ctypes.data)
+        c._keep = off   # the C side reads the host offsets during the call
+        return c
 
 
 def _launch_stream(stream, device, owned=()) -> int:
@@ -332,9 +355,10 @@ class Workspace:
         object.__setattr__(self, name, value)
 
 
-def alloc_aux(layer: LayerWeights, T: int, device) -> Aux:
+def alloc_aux(layer: LayerWeights, T: int, device, bias: Optional[Bias] = None) -> Aux:
     import torch
     E, k = layer.E, layer.k
+    nseq = 1 if bias is None else bias.nseq
     i32, f32 = torch.int32, torch.float32
     return Aux(logits=torch.empty((T, E), dtype=f32, device=device),
                topk_idx=torch.empty((T, k), dtype=i32, device=device),
@@ -344,8 +368,8 @@ def alloc_aux(layer: LayerWeights, T: int, device) -> Aux:
                csr_ptr=torch.empty(E + 1, dtype=i32, device=device),
                csr_tok=torch.empty(T * k, dtype=i32, device=device),
                csr_w=torch.empty(T * k, dtype=f32, device=device),
-               pstar=torch.empty(E, dtype=i32, device=device),
-               pstar_size=torch.empty(1, dtype=i32, device=device))
+               pstar=torch.empty(max(E, nseq * (bias.cap if bias else 0)), dtype=i32, device=device),
+               pstar_size=torch.empty(nseq, dtype=i32, device=device))
 
 
 def alloc_workspace(layer: LayerWeights, T: int, bias: Optional[Bias] = None, device=None,
@@ -356,16 +380,17 @@ def alloc_workspace(layer: LayerWeights, T: int, bias: Optional[Bias] = None, de
     ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
     ws = ws[off:off + n]
-    return Workspace(ws=ws, nbytes=n, aux=alloc_aux(layer, T, device) if with_aux else None)
+    return Workspace(ws=ws, nbytes=n, aux=alloc_aux(layer, T, device, bias) if with_aux else None)
 
 
-def _aux_sizes(layer: LayerWeights, T: int):
+def _aux_sizes(layer: LayerWeights, T: int, bias: Optional[Bias] = None):
     """Element count and dtype of each Aux field (include/moe_verify.h)."""
     E, k = layer.E, layer.k
+    nseq = 1 if bias is None else bias.nseq
     i32, f32 = ("int32",), ("float32",)
     return {"logits": (T * E, f32), "topk_idx": (T * k, i32), "topk_w": (T * k, f32), "union_size": (1, i32),
             "union_experts": (E, i32), "csr_ptr": (E + 1, i32), "csr_tok": (T * k, i32), "csr_w": (T * k, f32),
-            "pstar": (E, i32), "pstar_size": (1, i32)}
+            "pstar": (max(E, nseq * (bias.cap if bias else 0)), i32), "pstar_size": (nseq, i32)}
 
 
 def _check_workspace(wsp: Workspace, layer: LayerWeights, T: int, bias: Optional[Bias], dev) -> None:
@@ -373,7 +398,7 @@ def _check_workspace(wsp: Workspace, layer: LayerWeights, T: int, bias: Optional
     the C side trusts the byte count it is given.  The last passing
     (layer shape, T, bias cap, device) is remembered until a field of the
     workspace or of its aux is reassigned."""
-    key = (layer.H, layer.I, layer.E, layer.k, layer.wdtype, T, None if bias is None else bias.cap, dev)
+    key = (layer.H, layer.I, layer.E, layer.k, layer.wdtype, T, None if bias is None else (bias.cap, bias.nseq), dev)
     if getattr(wsp, "_valid_for", None) == key and (wsp.aux is None or getattr(wsp.aux, "_valid", False)):
         return
     need = workspace_bytes(layer, T, bias)
@@ -381,7 +406,7 @@ def _check_workspace(wsp: Workspace, layer: LayerWeights, T: int, bias: Optional
         raise ValueError(f"workspace holds {wsp.nbytes} bytes, this call needs {need}")
     _check_tensor(wsp.ws, "workspace.ws", ("uint8", "int8"), numel=wsp.nbytes, device=dev, at_least=True)
     if wsp.aux is not None:
-        for f, (n, dt) in _aux_sizes(layer, T).items():
+        for f, (n, dt) in _aux_sizes(layer, T, bias).items():
             t = getattr(wsp.aux, f)
             if t is not None:
                 _check_tensor(t, f"workspace.aux.{f}", dt, numel=n, device=dev, at_least=True)
@@ -407,7 +432,7 @@ def verify_layer(x, layer: LayerWeights, bias: Optional[Bias] = None, *, out=Non
         raise ValueError(f"x must be a device tensor, got {dev}")
     layer.validate(dev)
     if bias is not None:
-        _check_tensor(bias.w_conf, "bias.w_conf", ("float32",), numel=T, device=dev)
+        bias.check(T, dev)
     owned = []
     if workspace is None:
         workspace = alloc_workspace(layer, T, bias, device=dev)

@@ -31,6 +31,8 @@
 // per-(token, expert) rows of ydown and a combine in rank order.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 #include "route_block.h"
@@ -221,14 +223,16 @@ __device__ __forceinline__ void reduce_waves(f32x4 (&acc)[NT], f32x4 (*red)[NT][
     }
 }
 
+// Units per batch of the gate-up stream (wdtype 1 = bf16, 2 = fp8; nt column
+// tiles): enough loads in flight per wave, and few empty batch slots when the
+// item's units do not fill 8 waves evenly (bf16 with one column tile: 4,
+// measured against 2, 6 and 8 at H = 2880 and 4096).
+constexpr int gu_batch_units(int wdtype, int nt) { return wdtype == 2 ? (nt == 1 ? 2 : 1) : (nt <= 2 ? 4 : 2); }
+
 template <int WT, int NT>
 struct UnitCfg {
     static constexpr int KT = WT == 1 ? 64 : 32;                                    // k per tile
-    // units per batch: enough loads in flight per wave, and few empty batch
-    // slots when the item's units do not fill 8 waves evenly (bf16 with one
-    // column tile: 4, measured against 2, 6 and 8 at H = 2880 and 4096)
-    static constexpr int KU = WT == 1 ? (NT == 1 ? 2 : 1)
-                                      : (NT == 1 ? 4 : (NT == 2 ? 4 : 2));
+    static constexpr int KU = gu_batch_units(WT == 1 ? 2 : 1, NT);                  // units per batch
     static constexpr size_t USTEP = WT == 1 ? 2048 : 1024;                          // bytes per unit
     static constexpr int KSTEPS = WT == 1 ? 4 : 1;                                  // k-steps per unit
 };
@@ -251,10 +255,19 @@ constexpr int kGuMaxSplit = 4;  // most workgroups sharing one item's contractio
 // workgroup b takes part b % KS of it and holds only that part's slice of
 // the operand in LDS, and its partial gate and up sums go to gu_part for the
 // SwiGLU combine.
-template <int WT, int NT, bool SPLIT, bool FUSED, bool BLDS, int KS>
+// NGL > 0 (bf16, KS = 1): of every KU consecutive units, the last NGL take
+// their operand from global memory (where it stays L2-resident: every
+// workgroup reads the same few hundred KB) and only the others are staged in
+// LDS, so a contraction whose whole operand does not fit in LDS still runs in
+// one workgroup: no partial sums, no combine launch.  Which units come from
+// where is fixed by the unit's position in its batch, so the loads of a batch
+// are the same instructions every time.
+template <int WT, int NT, bool SPLIT, bool FUSED, bool BLDS, int KS, int NGL>
 __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     using C = UnitCfg<WT, NT>;
     constexpr int KU = C::KU;
+    static_assert(NGL == 0 || (WT == 0 && KS == 1 && BLDS && NGL < KU), "mixed operand: bf16, one part, LDS");
+    constexpr int KL = KU - NGL;  // units of every KU whose operand is staged in LDS
     using B = Batch<WT, NT, KU>;
     extern __shared__ __align__(16) unsigned char dyn_lds[];
     __shared__ f32x4 red[2][kGuWaves][NT][64];
@@ -272,29 +285,41 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     const int u0 = hk * nuh;                      // first unit of this workgroup's part
     constexpr int kspu = WT == 1 ? 4 : 1;         // k-steps of 32 per unit
     // dynamic LDS, in order: the activation operand (BLDS), the routing
-    // scratch and the token weights (FUSED).  With gu_async_x the operand
-    // has a region of its own and its loads fly while the routing runs;
-    // otherwise the routing scratch overlays the end of the operand region:
-    // the chunks below it are loaded while the routing runs, the rest after.
-    const int ksteps = nuh * kspu;                // k-steps of the part
-    const int nx = BLDS ? ksteps * 4 * cols : 0;  // 16-byte operand chunks
+    // scratch and the tokens' final selections (FUSED).  With gu_async_x the
+    // operand has a region of its own and its loads fly while the routing
+    // runs; otherwise the routing scratch overlays the end of the operand
+    // region: the chunks below it are loaded while the routing runs, the
+    // rest after.
+    const int nl = NGL == 0 ? nuh : (nuh / KU) * KL + min(nuh % KU, KL);  // units staged in LDS
+    const int cpu_ = kspu * 4 * cols;             // 16-byte operand chunks per unit
+    const int nx = BLDS ? nl * cpu_ : 0;          // 16-byte operand chunks in LDS
     const size_t xb_bytes = (size_t)nx * 16;
-    const size_t scr_bytes = FUSED ? (RouteScratch::bytes(T, p.k, E, kGuWaves) + 15) & ~(size_t)15 : 0;
+    const size_t scr_bytes =
+        FUSED ? (RouteScratch::bytes(T, p.k, E, kGuWaves, true, route_nseq(p)) + 15) & ~(size_t)15 : 0;
     const bool async_x = BLDS && p.gu_async_x != 0;
     // operand chunks that can be loaded before the routing is done
     const int early = async_x ? nx : (BLDS && xb_bytes >= scr_bytes ? (int)((xb_bytes - scr_bytes) / 16) : 0);
     u32x4 *xs = reinterpret_cast<u32x4 *>(dyn_lds);
     unsigned char *scr = dyn_lds + (async_x ? xb_bytes : (size_t)early * 16);
-    float *tw_lds = reinterpret_cast<float *>(
+    // [2 T k]: expert id, then gate weight (float bits), of rank j of token t
+    int *fin = reinterpret_cast<int *>(
         dyn_lds + (async_x ? xb_bytes + scr_bytes : (xb_bytes > scr_bytes ? xb_bytes : scr_bytes)));
-    // Direct global -> LDS copy of operand chunks [c0, c1) (one contiguous
-    // block, as the column stride equals the column count) by waves
-    // w0 .. w0 + nws - 1; lane l of a wave fills chunk i0 + l.
-    const uint16_t *xpart = p.xB + (size_t)u0 * kspu * 4 * cols * 8;  // the part's slice
+    // Direct global -> LDS copy of operand chunks [c0, c1) by waves
+    // w0 .. w0 + nws - 1; lane l of a wave fills chunk i0 + l.  LDS chunk i
+    // belongs to staged unit i / cpu_; staged unit li is unit
+    // (li / KL) KU + li % KL of the part (all of them when NGL = 0, where the
+    // copy is one contiguous block, as the column stride equals the column
+    // count).
+    const uint16_t *xpart = p.xB + (size_t)u0 * cpu_ * 8;  // the part's slice
+    auto src_chunk = [&](int i) -> int {
+        if (NGL == 0) return i;
+        const int li = i / cpu_, wi = i - li * cpu_;
+        return ((li / KL) * KU + li % KL) * cpu_ + wi;
+    };
     auto stage_x = [&](int w0, int nws, int c0, int c1) {
         if (w < w0) return;
         for (int i0 = c0 + (w - w0) * 64; i0 < c1; i0 += nws * 64)
-            if (i0 + lane < c1) load_lds16(xpart + (size_t)(i0 + lane) * 8, xs + i0);
+            if (i0 + lane < c1) load_lds16(xpart + (size_t)src_chunk(i0 + lane) * 8, xs + i0);
     };
 
     int nslots;
@@ -321,7 +346,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
             for (int c = w - T; c < nkt / 2; c += kGuWaves - T) load_lds16(sht + (size_t)c * 1024, &red[0][w][0][0]);
         }
         // routing, recomputed by every workgroup (bit-identical results)
-        block_route<kGuWaves * 64>(p, scr, sexp, tw_lds, &nslots_sh, blockIdx.x == 0);
+        block_route<kGuWaves * 64>(p, scr, sexp, nullptr, fin, &nslots_sh, blockIdx.x == 0);
         nslots = nslots_sh;
         if (early < nx) stage_x(0, kGuWaves, early, nx);
     } else {
@@ -407,10 +432,14 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
                 const int ks = kc * B::NS + q;
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    if (BLDS)
-                        bt.b[u][q][n] = xs[((kr * B::NS + q) * 4 + g) * cols + (coff[n] >> 3)];
-                    else
+                    if (BLDS && u < KL) {
+                        // staged unit of kr (units past the end read staged
+                        // unit 0: finite values, multiplied by zeros)
+                        const int li = NGL == 0 ? kr : (on ? (kr / KU) * KL + u : 0);
+                        bt.b[u][q][n] = xs[((li * B::NS + q) * 4 + g) * cols + (coff[n] >> 3)];
+                    } else {
                         bt.b[u][q][n] = *reinterpret_cast<const u32x4 *>(xb + (size_t)ks * bstep + coff[n]);
+                    }
                 }
             }
             bt.sc[u] = WT == 1 ? srow[kc] : 0.f;
@@ -462,7 +491,18 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
                 pp[t] = gv;
                 pp[T + t] = uv;
             } else {
-                const float wt = FUSED ? tw_lds[s * T + t] : p.tokw[(size_t)s * T + t];
+                float wt;
+                if (FUSED) {
+                    // gate weight of token t for the slot's expert (1 for the
+                    // always-on shared expert, 0 if the token is not routed
+                    // to it), from the token's final selection
+                    const int K = p.k, e = sexp[s];
+                    wt = e == E ? 1.f : 0.f;
+                    for (int j = 0; j < K; ++j)
+                        if (fin[t * K + j] == e) wt = __int_as_float(fin[T * K + t * K + j]);
+                } else {
+                    wt = p.tokw[(size_t)s * T + t];
+                }
                 const float hv = wt * (silu(gv) * uv);
                 const uint16_t hi = f32_to_bf16_rne(hv);
                 uint16_t *hb = p.hB + (size_t)s * I * cstride;
@@ -927,26 +967,52 @@ __global__ __launch_bounds__(256) void combine_kernel(VerifyParams p) {
 // of each must fit in LDS); the smallest that fits is taken.
 struct GuPlan {
     bool fused, blds, async_x;
-    int ks;
+    int ks;   // workgroups sharing one item's contraction
+    int ngl;  // units of every batch whose operand is read from global memory
     size_t dyn;
 };
 
+// Preference: the whole contraction per workgroup with the operand in LDS;
+// then (bf16) the whole contraction with the operand of 1 (or 2) of every
+// batch's units read from L2; then the contraction split over 2 or 4
+// workgroups (partial sums plus a combine launch); then the operand read
+// from L2 alone.  For each, the operand in a region of its own (its copy
+// overlaps the routing) before an overlay on the routing scratch.
 GuPlan plan_gateup(const VerifyParams &p) {
     const int nt = (p.cols + 15) / 16;
     const size_t stat = sizeof(float) * 4 * 2 * kGuWaves * nt * 64 + sizeof(int) * (kMaxExperts + 6);
     auto al = [](size_t v) { return (v + 15) & ~(size_t)15; };
-    const size_t scr = al(RouteScratch::bytes(p.T, p.k, p.E, kGuWaves));
-    const size_t tw = (size_t)p.max_slots * p.T * sizeof(float);
+    const size_t scr = al(RouteScratch::bytes(p.T, p.k, p.E, kGuWaves, true, route_nseq(p)));
+    const size_t fin = (size_t)p.T * p.k * 8;
     const int nunits = p.wdtype == 2 ? p.H / 128 : p.H / 32;
-    for (int ks = 1; ks <= kGuMaxSplit; ks *= 2) {
-        if (nunits % ks != 0) break;
-        const size_t xb = (size_t)(p.H / 32 / ks) * 4 * p.cols * 16;
+    const int kspu = p.wdtype == 2 ? 4 : 1;
+    const int ku = gu_batch_units(p.wdtype, nt);
+    auto try_plan = [&](int ks, int ngl, GuPlan &out) {
+        const int nuh = nunits / ks, kl = ku - ngl;
+        const int nl = ngl == 0 ? nuh : (nuh / ku) * kl + std::min(nuh % ku, kl);
+        const size_t xb = (size_t)nl * kspu * 4 * p.cols * 16;
         const size_t over = xb > scr ? xb : scr;
-        if (xb + scr + tw + stat <= kLdsPerCu) return {true, true, true, ks, xb + scr + tw};
-        if (over + tw + stat <= kLdsPerCu) return {true, true, false, ks, over + tw};
+        if (xb + scr + fin + stat <= kLdsPerCu) {
+            out = {true, true, true, ks, ngl, xb + scr + fin};
+            return true;
+        }
+        if (over + fin + stat <= kLdsPerCu) {
+            out = {true, true, false, ks, ngl, over + fin};
+            return true;
+        }
+        return false;
+    };
+    GuPlan pl{};
+    if (try_plan(1, 0, pl)) return pl;
+    if (p.wdtype == 1)
+        for (int ngl = 1; ngl < ku && ngl <= 2; ++ngl)
+            if (try_plan(1, ngl, pl)) return pl;
+    for (int ks = 2; ks <= kGuMaxSplit; ks *= 2) {
+        if (nunits % ks != 0) break;
+        if (try_plan(ks, 0, pl)) return pl;
     }
-    if (scr + tw + stat <= kLdsPerCu) return {true, false, false, 1, scr + tw};
-    return {false, false, false, 1, 0};
+    if (scr + fin + stat <= kLdsPerCu) return {true, false, false, 1, 0, scr + fin};
+    return {false, false, false, 1, 0, 0};
 }
 
 template <typename K>
@@ -965,12 +1031,20 @@ hipError_t launch_one(const VerifyParams &p, int n_cu, hipStream_t s, KernelEven
         VerifyParams q = p;
         q.gu_async_x = pl.async_x ? 1 : 0;
         if (pl.fused && pl.blds) {
-            if (pl.ks == 1) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 1>, q, pl.dyn, n_cu, s, ev);
-            if (pl.ks == 2) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 2>, q, pl.dyn, n_cu, s, ev);
-            return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 4>, q, pl.dyn, n_cu, s, ev);
+            if constexpr (WT == 0) {
+                if (pl.ks == 1 && pl.ngl == 1)
+                    return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 1, 1>, q, pl.dyn, n_cu, s, ev);
+                if constexpr (UnitCfg<WT, NT>::KU > 2)
+                    if (pl.ks == 1 && pl.ngl == 2)
+                        return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 1, 2>, q, pl.dyn, n_cu, s, ev);
+            }
+            if (pl.ngl != 0) return hipErrorInvalidValue;
+            if (pl.ks == 1) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 1, 0>, q, pl.dyn, n_cu, s, ev);
+            if (pl.ks == 2) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 2, 0>, q, pl.dyn, n_cu, s, ev);
+            return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 4, 0>, q, pl.dyn, n_cu, s, ev);
         }
-        if (pl.fused) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, false, 1>, q, pl.dyn, n_cu, s, ev);
-        return launch_gu(gateup_kernel<WT, NT, SPLIT, false, false, 1>, q, 0, n_cu, s, ev);
+        if (pl.fused) return launch_gu(gateup_kernel<WT, NT, SPLIT, true, false, 1, 0>, q, pl.dyn, n_cu, s, ev);
+        return launch_gu(gateup_kernel<WT, NT, SPLIT, false, false, 1, 0>, q, 0, n_cu, s, ev);
     } else {
         // one workgroup per compute unit; the work splits evenly over them.
         // When the row groups number at least 80% of the compute units, one

@@ -7,6 +7,8 @@
 
 namespace moe {
 
+constexpr int kMaxSegments = 64;  // sequences of one call (ragged verify, per-sequence bias)
+
 // Everything one verify-layer call needs, passed by value to every kernel.
 struct VerifyParams {
     int T, H, I, E, k, wdtype;
@@ -15,6 +17,8 @@ struct VerifyParams {
     int split;       // 1 if activations enter the products as a bf16 hi/lo pair
     int has_shared;  // always-on shared expert present
     int bias_on, cap;
+    int nseg;        // bias per sequence: tokens seg_off[s] .. seg_off[s+1]-1 form sequence s (0: pooled)
+    int seg_off[kMaxSegments + 1];
     int max_slots;   // min(E, T k) + has_shared: bound on the device slot count
     int gu_async_x;  // gate-up: operand staging runs alongside the routing (own LDS region)
     float alpha;
@@ -31,11 +35,11 @@ struct VerifyParams {
     float *topk_w;
     int *union_experts, *csr_ptr, *csr_tok;
     float *csr_w;
-    int *pstar;
-    int *union_size_out, *pstar_size_out;  // may be null
+    int *pstar;                            // [max(1, nseg), cap]: each sequence's P*, ascending
+    int *union_size_out, *pstar_size_out;  // may be null; pstar_size_out [max(1, nseg)]
 
     // workspace-only tables
-    int *meta;         // [0] union size U, [1] slots (U + shared), [2] |P*|
+    int *meta;         // [0] union size U, [1] slots (U + shared), [2] sum of |P*| over the sequences
     int *slot_expert;  // [slots] expert id per slot (E = shared expert)
     float *tokw;       // [slots * T] gate weight of token t in slot s (0 if not routed)
     int *tokpos;       // [slots * T] row of ydown for (slot, token), -1 if not routed
@@ -100,7 +104,6 @@ hipError_t launch_expand(ExpandArgs a, const float *P, const uint32_t *F, const 
                          int32_t *count, hipStream_t s);
 
 // Ragged verify: segment offsets by value, depth gating limits.
-constexpr int kMaxSegments = 64;
 constexpr int kGateMaxSeq = 64;
 constexpr int kGateMaxDepth = 64;
 constexpr int kGateMaxWords = 1024;  // (layer, expert) pairs <= 32768: 64 KB of uint16 counters

@@ -54,9 +54,14 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // tile at one tile per 16 tokens.
 bool split_mode(int T) { return 2 * T <= 16; }
 
+// Sequences with a preferred set of their own (1 when pooled).
+int bias_nseq(const moe_bias *bias) { return bias && bias->nseg > 0 ? bias->nseg : 1; }
+
 // The planning fields of the kernel parameters (what the gate-up plan reads).
-moe::VerifyParams plan_params(const moe_layer &L, int T) {
+moe::VerifyParams plan_params(const moe_layer &L, int T, const moe_bias *bias) {
     moe::VerifyParams p{};
+    p.bias_on = bias != nullptr;
+    p.nseg = bias && bias->nseg > 0 ? bias->nseg : 0;
     p.T = T;
     p.H = L.H;
     p.I = L.I;
@@ -71,9 +76,9 @@ moe::VerifyParams plan_params(const moe_layer &L, int T) {
     return p;
 }
 
-Layout make_layout(const moe_layer &L, int T) {
+Layout make_layout(const moe_layer &L, int T, const moe_bias *bias) {
     Layout o{};
-    o.ks = moe::gateup_ksplit(plan_params(L, T));
+    o.ks = moe::gateup_ksplit(plan_params(L, T, bias));
     const size_t E = L.E, k = L.k, H = L.H, I = L.I;
     const size_t slots = (size_t)std::min<long>(L.E, (long)T * L.k) + 1;
     const size_t cols = split_mode(T) ? 2 * T : T;
@@ -92,7 +97,7 @@ Layout make_layout(const moe_layer &L, int T) {
     o.csr_ptr = take((E + 1) * 4);
     o.csr_tok = take(T * k * 4);
     o.csr_w = take(T * k * 4);
-    o.pstar = take(E * 4);
+    o.pstar = take(std::max(E, (size_t)bias_nseq(bias) * (bias ? bias->cap : 0)) * 4);
     o.slot_expert = take(slots * 4);
     o.tokw = take(slots * T * 4);
     o.tokpos = take(slots * T * 4);
@@ -143,6 +148,16 @@ int validate_layer(const moe_layer *L, int T, const moe_bias *bias) {
         if (!(bias->alpha >= 0.f && bias->alpha < 1.f))
             return fail(MOE_EINVAL, "bias alpha=%g outside [0, 1)", (double)bias->alpha);
         if (!bias->w_conf) return fail(MOE_EINVAL, "bias w_conf is NULL");
+        if (bias->nseg < 0 || bias->nseg > moe::kMaxSegments)
+            return fail(MOE_EINVAL, "bias nseg=%d outside [0, %d]", bias->nseg, moe::kMaxSegments);
+        if (bias->nseg > 0) {
+            const int32_t *o = bias->seg_off;
+            if (!o) return fail(MOE_EINVAL, "bias seg_off is NULL with nseg=%d", bias->nseg);
+            if (o[0] != 0 || o[bias->nseg] != T)
+                return fail(MOE_EINVAL, "bias seg_off must run from 0 to T=%d", T);
+            for (int s = 1; s <= bias->nseg; ++s)
+                if (o[s] < o[s - 1]) return fail(MOE_EINVAL, "bias seg_off must not decrease");
+        }
     }
     return MOE_OK;
 }
@@ -155,7 +170,7 @@ const char *moe_last_error(void) { return g_err; }
 
 size_t moe_verify_workspace_bytes(const moe_layer *layer, int32_t T, const moe_bias *bias) {
     if (validate_layer(layer, T, bias) != MOE_OK) return 0;
-    return make_layout(*layer, T).total;
+    return make_layout(*layer, T, bias).total;
 }
 
 int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const moe_bias *bias, float *y,
@@ -166,16 +181,16 @@ int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const mo
     if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
     const moe_layer &L = *layer;
-    const Layout lay = make_layout(L, T);
+    const Layout lay = make_layout(L, T, bias);
     if (ws_bytes < lay.total)
         return fail(MOE_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, lay.total);
     if (reinterpret_cast<uintptr_t>(x) & 15 || reinterpret_cast<uintptr_t>(y) & 15)
         return fail(MOE_EINVAL, "x and y must be 16-byte aligned");
 
     char *w = static_cast<char *>(ws);
-    moe::VerifyParams p = plan_params(L, T);
-    p.bias_on = bias != nullptr;
+    moe::VerifyParams p = plan_params(L, T, bias);
     p.cap = bias ? bias->cap : 0;
+    for (int s = 0; p.nseg > 0 && s <= p.nseg; ++s) p.seg_off[s] = bias->seg_off[s];
     p.alpha = bias ? bias->alpha : 0.f;
     p.x = x;
     p.Wr = L.Wr;

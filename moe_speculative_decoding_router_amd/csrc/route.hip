@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(VerifyParams p) {
     // (slot, token) are only written, each by one thread, and go straight to
     // the workspace.
     __shared__ int sexp[kMaxExperts + 1];
-    block_route<kRouteThreads>(p, dyn, sexp, p.tokw, &nslots, true);
+    block_route<kRouteThreads>(p, dyn, sexp, p.tokw, nullptr, &nslots, true);
 }
 
 // Token chunks per expert: enough workgroups for the 256 compute units.
@@ -177,7 +177,9 @@ hipError_t launch_router(const VerifyParams &p, hipStream_t s, KernelEvents ev) 
     return per_wave <= 128 ? launch_router_up<2>(p, s, ev) : launch_router_up<4>(p, s, ev);
 }
 
-size_t route_lds_bytes(const VerifyParams &p) { return RouteScratch::bytes(p.T, p.k, p.E, kRouteThreads / 64); }
+size_t route_lds_bytes(const VerifyParams &p) {
+    return RouteScratch::bytes(p.T, p.k, p.E, kRouteThreads / 64, false, route_nseq(p));
+}
 
 hipError_t launch_route(const VerifyParams &p, hipStream_t s, KernelEvents ev) {
     const size_t lds = route_lds_bytes(p);

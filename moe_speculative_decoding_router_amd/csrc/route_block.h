@@ -225,6 +225,10 @@ __device__ __forceinline__ RankEntry wave_select(const float (&v)[kRouteNJ], con
     return wave_rank<NJ>(sel, key, v, v2, K, rbuf);
 }
 
+// Sequences with a preferred set of their own in a routing call (1 when the
+// bias is pooled over the call or off).
+__host__ __device__ inline int route_nseq(const VerifyParams &p) { return p.bias_on && p.nseg > 0 ? p.nseg : 1; }
+
 // LDS scratch of block_route, carved from a byte buffer for runtime T, k, E.
 struct RouteScratch {
     RankEntry *rank;            // [waves * 2 * kRankSlots]
@@ -235,17 +239,22 @@ struct RouteScratch {
     float *cg;                  // [T * k] w_b * softmax(l_b)_e of the selected e
     int *fin_i;                 // [T * k] final selection
     float *fin_w;               // [T * k]
-    float *g;                   // [E]
-    int *inP;                   // [E]
+    int *slot_off;              // [E] CSR offset of each union rank
+    unsigned *inP;              // [nseq * kTokWords] preferred set of each sequence, one bit per expert
     float *lam;                 // [T]
     int *wtot;                  // [2 * waves]
-    int *misc;                  // [4]: U, |P*|
+    int *misc;                  // [4]: U, sum of |P*|
 
-    __host__ __device__ static size_t bytes(int T, int k, int E, int waves) {
+    // ext_fin: the final selection (fin_i, fin_w) lives outside the scratch;
+    // nseq: sequences with a preferred set of their own (1 when pooled)
+    __host__ __device__ static size_t bytes(int T, int k, int E, int waves, bool ext_fin = false, int nseq = 1) {
         return (size_t)waves * 2 * kRankSlots * sizeof(RankEntry) + (((size_t)E * 8 + 15) & ~(size_t)15) + (size_t)T * kTokWords * 8 +
-               (size_t)T * k * 16 + (size_t)E * 8 + (size_t)T * 4 + (size_t)(2 * waves + 4) * 4 + 64;
+               (size_t)T * k * (ext_fin ? 8 : 16) + (size_t)E * 4 + (size_t)nseq * kTokWords * 4 + (size_t)T * 4 +
+               (size_t)(2 * waves + 4) * 4 + 64;
     }
-    __device__ void carve(unsigned char *base, int T, int k, int E, int waves) {
+    // fin: NULL, or [2 T k] words that receive the final selection (expert
+    // ids, then gate weights) and outlive the scratch
+    __device__ void carve(unsigned char *base, int T, int k, int E, int waves, int *fin, int nseq) {
         unsigned char *q = base;
         rank = reinterpret_cast<RankEntry *>(q);
         q += (size_t)waves * 2 * kRankSlots * sizeof(RankEntry);
@@ -259,14 +268,19 @@ struct RouteScratch {
         q += (size_t)T * k * 4;
         cg = reinterpret_cast<float *>(q);
         q += (size_t)T * k * 4;
-        fin_i = reinterpret_cast<int *>(q);
-        q += (size_t)T * k * 4;
-        fin_w = reinterpret_cast<float *>(q);
-        q += (size_t)T * k * 4;
-        g = reinterpret_cast<float *>(q);
+        if (fin) {
+            fin_i = fin;
+            fin_w = reinterpret_cast<float *>(fin + T * k);
+        } else {
+            fin_i = reinterpret_cast<int *>(q);
+            q += (size_t)T * k * 4;
+            fin_w = reinterpret_cast<float *>(q);
+            q += (size_t)T * k * 4;
+        }
+        slot_off = reinterpret_cast<int *>(q);
         q += (size_t)E * 4;
-        inP = reinterpret_cast<int *>(q);
-        q += (size_t)E * 4;
+        inP = reinterpret_cast<unsigned *>(q);
+        q += (size_t)nseq * kTokWords * 4;
         lam = reinterpret_cast<float *>(q);
         q += (size_t)T * 4;
         wtot = reinterpret_cast<int *>(q);
@@ -277,26 +291,30 @@ struct RouteScratch {
 
 // Routes the call with NTHREADS threads (NTHREADS >= E).  Results:
 //   LDS: sexp[s] expert of slot s (slot 0 = the shared expert E when there
-//        is one, then the union in ascending order), tw[s * T + t] gate
-//        weight of token t in slot s (0 if not routed), *nslots_lds.
-//   global (when write_global): topk_idx, topk_w, union, CSR, P* (ascending),
-//        meta, the slot tables (slot_expert, tokw, tokpos, tpos) of the FFN
-//        kernels.
+//        is one, then the union in ascending order), *nslots_lds; when fin
+//        is not NULL, fin[t * k + j] / fin[T * k + t * k + j] (as float) the
+//        expert and gate weight of rank j of token t.
+//   tw (when not NULL; LDS or global, written only): tw[s * T + t] gate
+//        weight of token t in slot s (0 if not routed).
+//   global (when write_global): topk_idx, topk_w, union, CSR, P* (each
+//        sequence's, ascending), meta, the slot tables (slot_expert, tokw,
+//        tokpos, tpos) of the FFN kernels.
 // The first pass gives token t to wave t % (NTHREADS / 64); waves without a
 // token wait at the barrier that ends it (the caller may hand them other work
-// before the call).  Barriers: pass 1, [bias: importance, preferred set,
-// re-selection], union scan, tables.
+// before the call).  Barriers: pass 1, [bias: importance and preferred set
+// per sequence, re-selection], union scan, tables.
 // NJ: row entries per lane the selections scan (>= ceil(E / 64)).
 template <int NTHREADS, int NJ>
 __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned char *scratch, int *sexp, float *tw,
-                                               int *nslots_lds, bool write_global) {
+                                               int *fin, int *nslots_lds, bool write_global) {
     static_assert(NTHREADS >= kMaxExperts, "the union scan gives every expert one thread");
     constexpr int NW = NTHREADS / 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int T = p.T, E = p.E, k = p.k;
     const bool bias = p.bias_on != 0;
+    const int nseq = route_nseq(p);
     RouteScratch sh;
-    sh.carve(scratch, T, k, E, NW);
+    sh.carve(scratch, T, k, E, NW, fin, nseq);
     RankEntry *rbuf = sh.rank + (size_t)w * 2 * kRankSlots;
     unsigned valid = 0u;  // slots of this lane inside the row
 #pragma unroll
@@ -318,6 +336,7 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     // ---- pass 1: top-k (k + 1 when the bias needs the (k+1)-th logit);
     //      lane r ends with the entry of rank r ----
     const int R = (bias && k < E) ? k + 1 : k;
+    if (tid == 0) sh.misc[1] = 0;  // sum of |P*|, counted after the first barrier
     for (int t = w; t < T; t += NW) {
         float v[kRouteNJ];
         load_logits(p.logits + (size_t)t * E, E, v);
@@ -362,26 +381,25 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     lds_barrier();
 
     if (bias) {
-        // ---- importance g_e (R4) of the first-pass selections, summed in
-        //      token order ----
-        for (int e = tid; e < E; e += NTHREADS) {
-            float g = 0.f;
-            for (int t = 0; t < T; ++t)
-                if ((sh.tbits0[t * kTokWords + (e >> 5)] >> (e & 31)) & 1u)
-                    for (int j = 0; j < k; ++j)
-                        if (sh.sel_i[t * k + j] == e) g += sh.cg[t * k + j];
-            sh.g[e] = g;
-            sh.inP[e] = 0;
-        }
-        lds_barrier();
-        // ---- preferred set P*: top-cap by (g desc, index asc) among g > 0 (R5) ----
-        if (w == 0) {
+        // ---- per sequence (the whole call when pooled, R16): importance
+        //      g_e (R4) of the sequence's first-pass selections, summed in
+        //      token order, and its preferred set P*, the top-cap by (g desc,
+        //      index asc) among g > 0 (R5).  Wave w takes sequences w,
+        //      w + NW, ...; lane l holds experts l + 64 j. ----
+        for (int sq = w; sq < nseq; sq += NW) {
+            const int t0 = p.nseg > 0 ? p.seg_off[sq] : 0;
+            const int t1 = p.nseg > 0 ? p.seg_off[sq + 1] : T;
             unsigned key[kRouteNJ];
             unsigned pos = 0u;
 #pragma unroll
             for (int j = 0; j < kRouteNJ; ++j) {
                 const int e = lane + 64 * j;
-                const float g = e < E ? sh.g[e] : 0.f;
+                float g = 0.f;
+                if (j < NJ && e < E)
+                    for (int t = t0; t < t1; ++t)
+                        if ((sh.tbits0[t * kTokWords + (e >> 5)] >> (e & 31)) & 1u)
+                            for (int r = 0; r < k; ++r)
+                                if (sh.sel_i[t * k + r] == e) g += sh.cg[t * k + r];
                 key[j] = float_ord(g);
                 if (e < E && g > 0.f) pos |= 1u << j;
             }
@@ -392,31 +410,38 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
             const int n = min(p.cap, npos);
             const unsigned sel = wave_topk_mask<NJ>(key, pos, n);
             const unsigned long long below = (1ull << lane) - 1ull;
+            unsigned *prow = sh.inP + sq * kTokWords;
             int base = 0;
 #pragma unroll
             for (int j = 0; j < kRouteNJ; ++j) {
                 if (j < NJ) {
                     const bool s = (sel >> j) & 1u;
                     const unsigned long long bal = __ballot(s);
-                    if (s) {
-                        sh.inP[lane + 64 * j] = 1;
-                        if (write_global) p.pstar[base + __popcll(bal & below)] = lane + 64 * j;
-                    }
+                    if (s && write_global) p.pstar[sq * p.cap + base + __popcll(bal & below)] = lane + 64 * j;
+                    if (lane < 2) prow[2 * j + lane] = (unsigned)(bal >> (32 * lane));
                     base += __popcll(bal);
                 }
             }
-            if (lane == 0) sh.misc[1] = n;
+            if (lane == 0) {
+                atomicAdd(&sh.misc[1], n);
+                if (write_global && p.pstar_size_out) p.pstar_size_out[sq] = n;
+            }
         }
         lds_barrier();
-        // ---- re-select on the biased logits; weights from the original (R6, R7) ----
+        // ---- re-select on the biased logits, each token with its own
+        //      sequence's P*; weights from the original (R6, R7) ----
         for (int t = w; t < T; t += NW) {
+            int sq = 0;
+            if (p.nseg > 0)
+                while (sq + 1 < p.nseg && p.seg_off[sq + 1] <= t) ++sq;
+            const unsigned *prow = sh.inP + sq * kTokWords;
             float v[kRouteNJ], vb[kRouteNJ];
             load_logits(p.logits + (size_t)t * E, E, v);
             const float lam = sh.lam[t];
 #pragma unroll
             for (int j = 0; j < kRouteNJ; ++j) {
                 const int e = lane + 64 * j;
-                vb[j] = (e < E && sh.inP[e]) ? __fadd_rn(v[j], lam) : v[j];
+                vb[j] = (e < E && ((prow[e >> 5] >> (e & 31)) & 1u)) ? __fadd_rn(v[j], lam) : v[j];
             }
             const RankEntry me = wave_select<NJ>(vb, v, valid, k, rbuf, true);
             const bool mine = lane < k;
@@ -441,7 +466,7 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     //      NJ groups of 64; slot = rank in the union, after the always-on
     //      shared expert (slot 0) when there is one ----
     const int so = p.has_shared ? 1 : 0;
-    int *slot_off = reinterpret_cast<int *>(sh.g);  // g is free again: CSR offset per union rank
+    int *slot_off = sh.slot_off;
     if (w == 0) {
         const unsigned long long below = (1ull << lane) - 1ull;
         // token masks of this lane's experts (lane + 64 j): the words of 8
@@ -518,7 +543,7 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
                 p.tpos[t * k + jj] = pos;
             }
         }
-        tw[s * T + t] = wt;
+        if (tw) tw[s * T + t] = wt;
         if (write_global) {
             p.tokw[(size_t)s * T + t] = wt;
             p.tokpos[(size_t)s * T + t] = pos;
@@ -526,7 +551,7 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     }
     if (p.has_shared && tid < T) {  // slot 0: the shared expert, weight 1 for every token
         if (tid == 0) sexp[0] = E;
-        tw[tid] = 1.f;
+        if (tw) tw[tid] = 1.f;
         if (write_global) {
             if (tid == 0) p.slot_expert[0] = E;
             p.tokw[tid] = 1.f;
@@ -536,13 +561,12 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     if (tid == 0) {
         *nslots_lds = U + p.has_shared;
         if (write_global) {
-            const int np = bias ? sh.misc[1] : 0;
             p.csr_ptr[U] = T * k;
             p.meta[0] = U;
             p.meta[1] = U + p.has_shared;
-            p.meta[2] = np;
+            p.meta[2] = bias ? sh.misc[1] : 0;
             if (p.union_size_out) p.union_size_out[0] = U;
-            if (p.pstar_size_out) p.pstar_size_out[0] = np;
+            if (!bias && p.pstar_size_out) p.pstar_size_out[0] = 0;
         }
     }
     lds_barrier();
@@ -551,13 +575,13 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
 // Routing with the selection loops sized for E.
 template <int NTHREADS>
 __device__ __forceinline__ void block_route(const VerifyParams &p, unsigned char *scratch, int *sexp, float *tw,
-                                            int *nslots_lds, bool write_global) {
+                                            int *fin, int *nslots_lds, bool write_global) {
     if (p.E <= 128)
-        block_route_nj<NTHREADS, 2>(p, scratch, sexp, tw, nslots_lds, write_global);
+        block_route_nj<NTHREADS, 2>(p, scratch, sexp, tw, fin, nslots_lds, write_global);
     else if (p.E <= 256)
-        block_route_nj<NTHREADS, 4>(p, scratch, sexp, tw, nslots_lds, write_global);
+        block_route_nj<NTHREADS, 4>(p, scratch, sexp, tw, fin, nslots_lds, write_global);
     else
-        block_route_nj<NTHREADS, kRouteNJ>(p, scratch, sexp, tw, nslots_lds, write_global);
+        block_route_nj<NTHREADS, kRouteNJ>(p, scratch, sexp, tw, fin, nslots_lds, write_global);
 }
 
 }  // namespace moe

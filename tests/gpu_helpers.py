@@ -61,12 +61,18 @@ def device_layer(wl: synth.Workload, layer: int, Wr: np.ndarray):
     return m.LayerWeights(H=wl.H, I=wl.I, E=wl.E, k=wl.k, wdtype=wl.wdtype, Wr=to_dev(Wr), **W)
 
 
+def bias_parts(bias_np):
+    """(cap, alpha, w_conf[, offsets]) -> cap, alpha, w_conf, offsets or None."""
+    cap, alpha, w_conf = bias_np[:3]
+    return cap, alpha, w_conf, (bias_np[3] if len(bias_np) > 3 else None)
+
+
 def run_layer(layer_w, x: np.ndarray, bias_np=None):
     import torch
     bias = None
     if bias_np is not None:
-        cap, alpha, w_conf = bias_np
-        bias = m.Bias(cap=cap, alpha=alpha, w_conf=to_dev(w_conf.astype(np.float32)))
+        cap, alpha, w_conf, offsets = bias_parts(bias_np)
+        bias = m.Bias(cap=cap, alpha=alpha, w_conf=to_dev(w_conf.astype(np.float32)), offsets=offsets)
     y, aux = m.verify_layer(to_dev(x), layer_w, bias)
     torch.cuda.synchronize()
     out = {f: getattr(aux, f).cpu().numpy() for f in m.Aux.__dataclass_fields__}
@@ -83,23 +89,32 @@ def check_routing(out, k, E, bias_np=None, x=None, Wr=None):
         assert np.abs(logits - ref).max() <= 1e-5 * np.abs(ref).max(), "router logits"
     if bias_np is None:
         r = omoe.route(logits, k)
+        assert int(out["pstar_size"][0]) == 0, "P* size without the bias"
     else:
-        cap, alpha, w_conf = bias_np
-        r_own = omoe.route(logits, k, w_conf=w_conf, cap=cap, alpha=alpha)
-        npst = int(out["pstar_size"][0])
-        gpu_pstar = out["pstar"][:npst]
-        # P* depends on exp(): compare it where the importance gap at the cap
-        # boundary is clear; the remaining steps are checked given the device P*
-        g = r_own.bias.g
-        order = omoe.order_desc(g)
-        pos = [e for e in order if g[e] > 0]
-        if len(pos) > cap:
-            gap = g[pos[cap - 1]] - g[pos[cap]]
-            if gap > 1e-5 * g.max():
-                assert np.array_equal(np.sort(gpu_pstar), np.sort(r_own.bias.pstar)), "P*"
-        else:
-            assert np.array_equal(np.sort(gpu_pstar), np.sort(r_own.bias.pstar)), "P*"
-        r = omoe.route(logits, k, w_conf=w_conf, cap=cap, alpha=alpha, pstar=gpu_pstar)
+        cap, alpha, w_conf, offsets = bias_parts(bias_np)
+        r_own = omoe.route(logits, k, w_conf=w_conf, cap=cap, alpha=alpha, offsets=offsets)
+        # one preferred set per sequence (one for the pooled call)
+        own_sets = r_own.bias.pstar if offsets is not None else [r_own.bias.pstar]
+        own_g = r_own.bias.g if offsets is not None else r_own.bias.g[None]
+        dev_sets = []
+        for sq, (ps_own, g) in enumerate(zip(own_sets, own_g)):
+            npst = int(out["pstar_size"][sq])
+            gpu_pstar = out["pstar"][sq * cap:sq * cap + npst]
+            assert np.array_equal(gpu_pstar, np.sort(gpu_pstar)), "P* ascending"
+            # P* depends on exp(): compare it where the importance gap at the
+            # cap boundary is clear; the remaining steps are checked given the
+            # device P*
+            order = omoe.order_desc(g)
+            pos = [e for e in order if g[e] > 0]
+            if len(pos) > cap:
+                gap = g[pos[cap - 1]] - g[pos[cap]]
+                if gap > 1e-5 * g.max():
+                    assert np.array_equal(gpu_pstar, np.sort(ps_own)), f"P* of sequence {sq}"
+            else:
+                assert np.array_equal(gpu_pstar, np.sort(ps_own)), f"P* of sequence {sq}"
+            dev_sets.append(gpu_pstar)
+        r = omoe.route(logits, k, w_conf=w_conf, cap=cap, alpha=alpha,
+                       pstar=dev_sets if offsets is not None else dev_sets[0], offsets=offsets)
     assert np.array_equal(out["topk_idx"], r.topk_idx), "top-k"
     assert np.abs(out["topk_w"] - r.topk_w).max() <= 1e-6, "gate weights"
     U = omoe.expert_union(r.topk_idx)

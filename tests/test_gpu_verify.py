@@ -2,6 +2,8 @@
 routing, union and CSR bit for bit (given the device logits), outputs within
 the format's tolerance, at small sizes spanning several tiles and ragged
 tails, and at the full configuration sizes."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -222,13 +224,27 @@ def test_bf16_all_limits():
 @pytest.mark.parametrize("T", [20, 32, 64])
 def test_bf16_wide_operand(T):
     """H = 4096 with 20, 32 and 64 token columns: the activation operand does
-    not fit in LDS whole, so the contraction of each item is split over 2
-    (T = 20) or 4 (T = 32) workgroups and finished by the SwiGLU combine; at
-    T = 64 no slice fits and the operand is read from L2 with the tail items
-    handed out by tickets (I = 1024 gives the 16 experts enough items)."""
+    not fit in LDS whole.  At T = 20 each workgroup still runs whole items,
+    with the operand of one unit in four read from L2; at T = 32 the
+    contraction of each item is split over 4 workgroups and finished by the
+    SwiGLU combine; at T = 64 no slice fits and the operand is read from L2
+    with the tail items handed out by tickets (I = 1024 gives the 16 experts
+    enough items)."""
     I = 1024 if T == 64 else 256
     log(f"case bf16 H=4096 I={I} T={T}")
     wl = small("qwen3_bf16", H=4096, I=I, E=16, k=4, T=T, rate=0.05, cid=14)
+    verify_workload(wl)
+
+
+@pytest.mark.parametrize("H,T", [(4096, 24), (2880, 24), (2880, 32), (2048, 40)])
+def test_bf16_operand_partly_from_l2(H, T):
+    """Whole items per workgroup with part of the activation operand read from
+    L2: H = 4096, T = 24 reads two units in four from L2; H = 2880 (90
+    units, not a multiple of the 4-unit batch) reads one in four at T = 24
+    and two in four at T = 32, so the last batch of every item is partial;
+    H = 2048, T = 40 (three column tiles, 2-unit batches) reads one in two."""
+    log(f"case bf16 H={H} T={T} operand partly from L2")
+    wl = small("qwen3_bf16", H=H, I=256, E=16, k=4, T=T, rate=0.05, cid=17)
     verify_workload(wl)
 
 
@@ -342,10 +358,22 @@ def test_workspace_error_through_real_library():
     from gpu_helpers import device_layer
     lw = device_layer(wl, 0, Wr)
     wsp = m.alloc_workspace(lw, 5)
-    wsp.nbytes -= 1024
-    with pytest.raises(m.MoeError) as ei:
-        m.verify_layer(to_dev(x), lw, workspace=wsp)
-    assert ei.value.code == -3
+    xd = to_dev(x)
+    y = torch.empty_like(xd)
+    # the binding refuses a workspace below what the call needs ...
+    short = m.Workspace(ws=wsp.ws, nbytes=wsp.nbytes - 1024, aux=wsp.aux)
+    with pytest.raises(ValueError, match="workspace"):
+        m.verify_layer(xd, lw, workspace=short)
+    # ... and so does the C ABI itself, before anything is enqueued
+    L = lw._c()
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = m.lib().moe_verify_layer(ctypes.byref(L), xd.data_ptr(), 5, None, y.data_ptr(), None,
+                                  wsp.ws.data_ptr(), wsp.nbytes - 1024, stream)
+    assert rc == -3 and b"workspace" in m.lib().moe_last_error()
+    rc = m.lib().moe_verify_layer(ctypes.byref(L), xd.data_ptr(), 5, None, y.data_ptr(), None,
+                                  wsp.ws.data_ptr(), wsp.nbytes, stream)
+    torch.cuda.synchronize()
+    assert rc == 0
 
 
 # ---------------------------------------------------------------------------
@@ -377,6 +405,58 @@ def test_full_qwen3_batch4_layer(bias_on):
         bias = (16, 0.5, rng.random(wl.T).astype(np.float32))
     out, r = verify_workload(wl, bias_np=bias)
     log(f"    union {int(out['union_size'][0])} experts")
+
+
+def test_full_qwen3_batch4_layer_bias_per_sequence():
+    """The batched layer with the reuse bias computed per sequence (the 4
+    sequences of 5 tokens each have their own importance and preferred set)
+    on layers 0 and 5, against the oracle; no sequence's expert set grows."""
+    wl = synth.WORKLOADS["qwen3_batch4_bf16"]
+    rng = synth.rng_for(0, wl.cid, 999)
+    w_conf = rng.random(wl.T).astype(np.float32)
+    offsets = [0, 5, 10, 15, 20]
+    for layer in (0, 5):
+        log(f"case full qwen3_batch4 layer {layer} (T=20), bias per sequence")
+        out, r = verify_workload(wl, layer=layer, bias_np=(16, 0.5, w_conf, offsets))
+        idx0 = omoe.topk(out["logits"], wl.k)
+        for s in range(4):
+            a, b = offsets[s], offsets[s + 1]
+            assert set(r.topk_idx[a:b].ravel()) <= set(idx0[a:b].ravel())
+        pooled = omoe.route(out["logits"], wl.k, w_conf=w_conf, cap=16, alpha=0.5)
+        log(f"    union {int(out['union_size'][0])} experts per sequence, "
+            f"{len(omoe.expert_union(pooled.topk_idx))} pooled, {len(omoe.expert_union(idx0))} unbiased")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_bias_random_sequences(seed):
+    """Random segmentations (empty sequences included) with the per-sequence
+    bias, on bf16 layers (routing fused into the gate-up kernel) and on
+    float32 layers (the standalone route kernel)."""
+    rng = np.random.default_rng(900 + seed)
+    T = int(rng.integers(2, 40))
+    S = int(rng.integers(1, min(T, 9) + 1))
+    cuts = np.sort(rng.integers(0, T + 1, size=S - 1))
+    offsets = [0] + [int(c) for c in cuts] + [T]
+    w_conf = rng.random(T).astype(np.float32)
+    if seed % 2 == 0:
+        wl = small("qwen3_bf16", T=T, H=512, I=256, E=int(rng.choice([16, 64, 160])), k=int(rng.integers(1, 9)),
+                   n_seq=1, cid=30 + seed)
+        cap = int(rng.integers(wl.k, min(wl.E, 3 * wl.k) + 1))
+        log(f"case bf16 T={T} E={wl.E} k={wl.k} cap={cap} offsets={offsets}")
+        verify_workload(wl, bias_np=(cap, 0.5, w_conf, offsets))
+    else:
+        H, I, E, k = 64, 32, int(rng.choice([8, 100, 512])), int(rng.integers(1, 9))
+        cap = int(rng.integers(k, min(E, 3 * k) + 1))
+        log(f"case f32 T={T} E={E} k={k} cap={cap} offsets={offsets}")
+        x = rng.standard_normal((T, H)).astype(np.float32)
+        Wr = (0.5 * rng.standard_normal((E, H))).astype(np.float32)
+        Wgu = (0.05 * rng.standard_normal((E, 2 * I, H))).astype(np.float32)
+        Wd = (0.05 * rng.standard_normal((E, H, I))).astype(np.float32)
+        bias = (cap, 0.7, w_conf, offsets)
+        out = run_layer(f32_layer(Wr, Wgu, Wd, k), x, bias)
+        r = check_routing(out, k, E, bias, x, Wr)
+        y_ref = omoe.moe_layer(x, r.topk_idx, r.topk_w, f32_expert_fn(Wgu, Wd, I))
+        check_output(out, y_ref, "f32", split=True)
 
 
 @pytest.mark.parametrize("part", [0, 1])
