@@ -42,7 +42,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--model-layers", type=int, default=0,
                     help="MoE layers verified per step (default: the model's MoE layer count)")
-    ap.add_argument("--workload", default="qwen3_bf16")
+    ap.add_argument("--workload", default="qwen3_batch4_bf16",
+                    help="headline workload (default: the largest one-GPU configuration, 4 sequences x 5 tokens)")
+    ap.add_argument("--also", default="qwen3_bf16,deepseek_fp8,gptoss_bf16",
+                    help="comma-separated workloads measured after the headline and reported under 'workloads' "
+                         "('' for none)")
+    ap.add_argument("--no-calib", action="store_true", help="skip the wide-range cost-model calibration")
     ap.add_argument("--layers", type=int, default=8, help="distinct layers cycled by the steps")
     ap.add_argument("--trees", type=int, default=1, help="draft trees selected per step")
     ap.add_argument("--bias", action="store_true", help="turn the reuse-aware soft bias on")
@@ -71,12 +76,6 @@ def main() -> int:
     import synth
 
     dev = torch.device("cuda:0")
-    wl = synth.WORKLOADS[args.workload]
-    T, L = wl.T, max(1, args.layers)
-
-    def to_dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
     if args.copy_probe_mib > 0:
         nb = args.copy_probe_mib << 20
         src = torch.ones(nb, dtype=torch.uint8, device=dev)
@@ -87,35 +86,64 @@ def main() -> int:
         err(f"[bench] copy probe: {nb} bytes device to device")
         del src, dst
 
+    head = measure_workload(m, synth, args, args.workload, dev, headline=True)
+    subs = {}
+    for name in [w for w in args.also.split(",") if w and w != args.workload]:
+        subs[name] = measure_workload(m, synth, args, name, dev, headline=False)
+    out = head.pop("_line")
+    out["read_stream"] = read_stream(m, torch, dev)
+    if subs:
+        out["workloads"] = subs
+    if not args.no_cpu_baseline:
+        wl = synth.WORKLOADS[args.workload]
+        be = m.expert_bytes(wl.H, wl.I, wl.wdtype)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, be, 1 if wl.shared else 0)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def measure_workload(m, synth, args, name, dev, headline):
+    """Times `args.steps` verify steps of workload `name` (after
+    `args.warmup` untimed ones) and returns its record.  The headline record
+    carries the bench line's fields under '_line'; every record carries the
+    per-kernel figures, its roofline fraction and the cost-model fit."""
+    import numpy as np
+    import torch
+
+    wl = synth.WORKLOADS[name]
+    if wl.wdtype == "f32":
+        raise SystemExit("bench.py measures the bf16/fp8 workloads")
+    T, L = wl.T, max(1, args.layers)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
     # ---------------- inputs (seeded, synthetic, resident in HBM) ----------------
     err(f"[bench] building {L} {wl.name} layers on the device")
     layers = []
     for l in range(L):
         x, _, Wr = synth.layer_inputs(wl, l)
-        if wl.wdtype == "f32":
-            raise SystemExit("bench.py measures the bf16/fp8 workloads")
         W = m.pack_layer_tensors(synth.fill_layer_device(wl, l, dev), wl.wdtype)
         torch.cuda.synchronize()
         lw = m.LayerWeights(H=wl.H, I=wl.I, E=wl.E, k=wl.k, wdtype=wl.wdtype, Wr=to_dev(Wr), **W)
         layers.append((lw, to_dev(x)))
     bias = None
-    if args.bias:
+    if args.bias and headline:
         rng = synth.rng_for(0, wl.cid, 999)
         bias = m.Bias(cap=2 * wl.k, alpha=0.5, w_conf=to_dev(rng.random(T).astype(np.float32)))
-    trees = synth.draft_trees(seed=0, nt=args.trees, n_layers=MODEL_LAYERS[wl.name], E=wl.E, k=wl.k)
+    ML = args.model_layers or MODEL_LAYERS[wl.name]
+    trees = synth.draft_trees(seed=0, nt=args.trees, n_layers=ML, E=wl.E, k=wl.k)
     P_d, F_d = to_dev(trees.P), to_dev(trees.F.view(np.int32))
     S_d = torch.empty((args.trees, 4), dtype=torch.int32, device=dev)
     wsp = m.alloc_workspace(layers[0][0], T, bias, device=dev)
     y = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    ML = args.model_layers or MODEL_LAYERS[wl.name]
-
-    def step(i):
+    def step(i, evs=None):
         m.select_drafts(trees.parent, P_d, F_d, 4, out=S_d)
         for j in range(ML):
             lw, x = layers[(i * ML + j) % L]
-            m.verify_layer(x, lw, bias, out=y, workspace=wsp)
+            m.verify_layer(x, lw, bias, out=y, workspace=wsp, events=None if evs is None else evs.get((i, j)))
 
     # union size per layer -> unique-expert bytes
     be = m.expert_bytes(wl.H, wl.I, wl.wdtype)
@@ -129,7 +157,7 @@ def main() -> int:
         U.append(int(wsp.aux.union_size.item()))
     n_sh = 1 if wl.shared else 0
     bytes_layer = [(u + n_sh) * be for u in U]
-    err(f"[bench] unions per layer: {U}")
+    err(f"[bench] {wl.name}: unions per layer: {U}")
 
     # ---------------- timed region ----------------
     # Every EV_STRIDE-th verify call of the region (the stride is coprime with
@@ -149,24 +177,17 @@ def main() -> int:
     for e in (e for row in evs.values() for e in row):   # torch creates the HIP event at its first record
         e.record(stream)
     torch.cuda.synchronize()
-
-    def timed_step(i):
-        m.select_drafts(trees.parent, P_d, F_d, 4, out=S_d)
-        for j in range(ML):
-            lw, x = layers[(i * ML + j) % L]
-            m.verify_layer(x, lw, bias, out=y, workspace=wsp, events=evs.get((i, j)))
-
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(args.steps):
-        timed_step(i)
+        step(i, evs)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ms_step = total_ms / args.steps
     total_bytes = sum(bytes_layer[(i * ML + j) % L] for i in range(args.steps) for j in range(ML))
     value = total_bytes / (total_ms * 1e-3) / 1e9
-    err(f"[bench] {args.steps} steps x {ML} layers in {total_ms:.3f} ms -> {ms_step * 1e3:.1f} us/step, "
+    err(f"[bench] {wl.name}: {args.steps} steps x {ML} layers in {total_ms:.3f} ms -> {ms_step * 1e3:.1f} us/step, "
         f"{ms_step * 1e3 / ML:.1f} us/layer, {value:.0f} GB/s")
     # kernel durations [sampled calls, stages] in ms
     stage_ms = np.array([[evs[c][2 * q].elapsed_time(evs[c][2 * q + 1]) for q in range(NS)] for c in sampled])
@@ -182,80 +203,117 @@ def main() -> int:
     # for matrix-core weights; a stage without a kernel records its events
     # back to back, which reads a few microseconds)
     call_us = (stage_ms[:, 0] + stage_ms[:, 2] + stage_ms[:, 3]) * 1e3
-
-    out_extra = {"read_stream": read_stream(m, torch, dev),
-                 "select_4096_trees": select_timing(m, synth, wl, dev, stream, nt=4096)}
-    if wl.n_seq > 1 and not args.no_ab:
-        out_extra["config_ab"] = config_ab(m, synth, wl, layers, dev)
-
-    # ---------------- CPU oracle baseline (bounded sample) ----------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds, U[0], be, n_sh)
-
-    out = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.wdtype,
-        "data": "synthetic (seeded structured router logits, planted router, counter-generated weights)",
-        "config": {"workload": wl.name, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k, "T": T,
-                   "shared_expert": wl.shared, "moe_layers_per_step": ML, "distinct_layers_cycled": L,
-                   "trees_per_step": args.trees, "bias": bool(args.bias)},
-        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+    kernels = {}
+    for q, kname in enumerate(m.STAGE_NAMES):
+        if kname not in kbytes:
+            continue
+        gbs = float(kbytes[kname].sum() / (stage_ms[:, q].sum() * 1e-3) / 1e9)
+        kernels[kname] = {"avg_us": round(float(stage_ms[:, q].mean() * 1e3), 2), "launches": len(lidx),
+                          "bytes_per_launch": round(float(kbytes[kname].mean())), "GBs": round(gbs, 1),
+                          "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    gu = kernels["gate_up"]
+    ffn_gbs = float(ffn_bytes.sum() / (ffn_ms.sum() * 1e-3) / 1e9)
+    rec = {
+        "workload": wl.name, "T": T, "dtype": wl.wdtype,
         "unique_experts_per_layer": round(float(np.mean(U)), 2),
         "unique_expert_MB_per_layer": round(float(np.mean(bytes_layer)) / 1e6, 1),
-        "us_per_step": round(ms_step * 1e3, 2),
         "verify_us_per_layer_incl_select": round(ms_step * 1e3 / ML, 2),
+        "GBs": round(value, 1), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "ms_per_step": round(ms_step, 5), "moe_layers_per_step": ML,
         "verify_kernel_us_per_layer_p10_p50_p90": [round(float(v), 2) for v in np.percentile(call_us, [10, 50, 90])],
+        "kernels": kernels,
+        "ffn_us_per_layer": round(float(ffn_ms.mean() * 1e3), 2),
+        "ffn_GBs": round(ffn_gbs, 1), "ffn_frac_of_hbm_peak": round(ffn_gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"kernel": "gateup_kernel", "bound": "hbm", "achieved": gu["GBs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gu["GBs"] / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(wl.name, "gate_up")},
+        "kernel_events": f"start/end events on 1 in {EV_STRIDE} verify calls of the timed region "
+                         f"({len(sampled)} calls)",
     }
-    # the kernels every bf16/fp8 call runs (the route stage runs a kernel only
-    # when the routing scratch exceeds LDS; combine only for float32 weights)
-    kernels = {}
-    for q, name in enumerate(m.STAGE_NAMES):
-        if name not in kbytes:
-            continue
-        kernels[name] = {"avg_us": round(float(stage_ms[:, q].mean() * 1e3), 2), "launches": len(lidx),
-                         "bytes_per_launch": round(float(kbytes[name].mean())),
-                         "GBs": round(float(kbytes[name].sum() / (stage_ms[:, q].sum() * 1e-3) / 1e9), 1)}
-    out["kernels"] = kernels
-    out.update(out_extra)
-    # Cost model of the expansion step ([S2-MoE] component 1, Fig. 6): verify
-    # latency = a + T_exp * (unique experts).  Least-squares fit over the
-    # sampled calls (router + gate-up + down kernel time against U).
-    ver_us = (stage_ms[:, 0] + stage_ms[:, 2] + stage_ms[:, 3]) * 1e3
-    u_s = np.array([U[q] + n_sh for q in lidx], dtype=np.float64)
-    if np.ptp(u_s) > 0:
-        b_fit, a_fit = np.polyfit(u_s, ver_us, 1)
-        pred = a_fit + b_fit * u_s
-        r2 = 1.0 - float(((ver_us - pred) ** 2).sum() / ((ver_us - ver_us.mean()) ** 2).sum())
-        out["cost_model"] = {"t_exp_us_per_unique_expert": round(float(b_fit), 3),
-                             "intercept_us": round(float(a_fit), 2), "r2": round(r2, 4),
-                             "mape": round(float(np.mean(np.abs(ver_us - pred) / ver_us)), 4),
-                             "calls": len(lidx), "unique_experts_range": [int(u_s.min()), int(u_s.max())]}
-    out["kernel_events"] = f"start/end events on 1 in {EV_STRIDE} verify calls of the timed region ({len(sampled)} calls)"
-    out["ffn_us_per_layer"] = round(float(ffn_ms.mean() * 1e3), 2)
-    out["ffn_GBs"] = round(float(ffn_bytes.sum() / (ffn_ms.sum() * 1e-3) / 1e9), 1)
-    out["ffn_frac_of_hbm_peak"] = round(out["ffn_GBs"] / HBM_PEAK_GBS, 4)
-    gu = kernels["gate_up"]
-    out["roofline"] = {"kernel": "gateup_kernel (router top-k + union + gate/up SwiGLU over the union experts)",
-                       "bound": "hbm", "achieved": gu["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": round(gu["GBs"] / HBM_PEAK_GBS, 4),
-                       "traffic": measured_traffic(wl.name, "gate_up"),
-                       "bytes_per_launch": gu["bytes_per_launch"], "avg_us": gu["avg_us"]}
-    if args.ablation:
-        out["ablation"] = ablation(m, synth, wl, layers, ML, dev, stream)
-    if cpu is not None:
-        out["cpu_baseline"] = cpu
-    print(json.dumps(out), flush=True)
-    return 0
+    if not args.no_calib:
+        rec["cost_model"] = calibrate_cost_model(m, synth, wl, layers, dev)
+    if headline:
+        rec["select_4096_trees"] = select_timing(m, synth, wl, dev, stream, nt=4096)
+        if wl.n_seq > 1 and not args.no_ab:
+            rec["config_ab"] = config_ab(m, synth, wl, layers, dev)
+        if args.ablation:
+            rec["ablation"] = ablation(m, synth, wl, layers, ML, dev, stream)
+        line = {
+            "metric": METRIC,
+            "value": round(value, 1),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": wl.wdtype,
+            "data": "synthetic (seeded structured router logits, planted router, counter-generated weights)",
+            "config": {"workload": wl.name, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k, "T": T,
+                       "sequences": wl.n_seq, "shared_expert": wl.shared, "moe_layers_per_step": ML,
+                       "distinct_layers_cycled": L, "trees_per_step": args.trees, "bias": bias is not None},
+            "roofline": dict(rec["roofline"], kernel="gateup_kernel (router top-k + union + gate/up SwiGLU over "
+                                                     "the union experts)",
+                             bytes_per_launch=gu["bytes_per_launch"], avg_us=gu["avg_us"]),
+        }
+        line.update({k: v for k, v in rec.items() if k not in ("roofline", "ms_per_step", "dtype", "T")})
+        rec["_line"] = line
+    del layers, wsp, y
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def calibrate_cost_model(m, synth, wl, layers, dev, Ts=(1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20), reps=5):
+    """Cost model of the expansion step ([S2-MoE] component 1, Fig. 6):
+    verify latency = a + T_exp * (unique experts).  The verify kernels
+    (router + gate-up + down, start/end events, median of `reps` calls) run
+    on the resident layers for T = 1 .. 20 tokens of one sequence, each layer
+    with the router planted for those tokens, so the union spans a wide
+    range; least-squares fit of the kernel time against the number of
+    experts streamed (union + shared expert)."""
+    import dataclasses
+    import numpy as np
+    import torch
+
+    NS = m.NUM_STAGES
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * NS)]
+    for e in ev:  # torch creates the HIP event at its first record
+        e.record()
+    torch.cuda.synchronize()
+    n_sh = 1 if wl.shared else 0
+    us_all, u_all, t_all = [], [], []
+    for T in Ts:
+        for l, (lw, _) in enumerate(layers):
+            x, _, Wr = synth.layer_inputs(wl, l, T=T, n_seq=1)
+            lw2 = dataclasses.replace(lw, Wr=torch.from_numpy(Wr).to(dev))
+            xd = torch.from_numpy(x).to(dev)
+            ws = m.alloc_workspace(lw2, T, None, device=dev)
+            y = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
+            times = []
+            for _ in range(reps + 1):
+                m.verify_layer(xd, lw2, out=y, workspace=ws, events=ev)
+                torch.cuda.synchronize()
+                times.append(sum(ev[2 * q].elapsed_time(ev[2 * q + 1]) for q in (0, 2, 3)) * 1e3)
+            us_all.append(float(np.median(times[1:])))
+            u_all.append(int(ws.aux.union_size.item()) + n_sh)
+            t_all.append(T)
+    us, u = np.array(us_all), np.array(u_all, dtype=np.float64)
+    b, a = np.polyfit(u, us, 1)
+    pred = a + b * u
+    r2 = 1.0 - float(((us - pred) ** 2).sum() / ((us - us.mean()) ** 2).sum())
+    mape = float(np.mean(np.abs(us - pred) / us))
+    err(f"[bench] {wl.name}: cost model T_exp {b:.3f} us/expert, intercept {a:.2f} us, R2 {r2:.4f}, "
+        f"MAPE {mape:.4f}, experts {int(u.min())}..{int(u.max())}")
+    return {"t_exp_us_per_unique_expert": round(float(b), 3), "intercept_us": round(float(a), 2),
+            "r2": round(r2, 4), "mape": round(mape, 4), "points": len(us_all),
+            "tokens": list(Ts), "experts_streamed_range": [int(u.min()), int(u.max())],
+            "note": "verify kernel time (router + gate-up + down) against experts streamed, T = 1..20 "
+                    "tokens of one sequence on each cycled layer, median of 5 calls"}
 
 
 def ablation(m, synth, wl, layers, ML, dev, stream, n_trees=8, n_layers=8):
@@ -381,8 +439,8 @@ def config_ab(m, synth, wl, layers, dev, reps=15):
     with the router planted for the arm's tokens: width against depth at
     T = 2 ([W-vs-D] section 1: two consecutive tokens of one sequence, whose
     routes are correlated, against one token from each of two sequences) and
-    the reuse bias off and on at the workload's T ([S2-MoE] component 2,
-    cap 2k, alpha 0.5).  Reports unique experts and the verify kernel time
+    the reuse bias off, on pooled over the call and on per sequence at the
+    workload's T ([S2-MoE] component 2, cap 2k, alpha 0.5).  Reports unique experts and the verify kernel time
     (router + gate-up + down events, median of reps calls) per layer."""
     import dataclasses
     import numpy as np
@@ -391,7 +449,7 @@ def config_ab(m, synth, wl, layers, dev, reps=15):
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    def arm(T, n_seq, with_bias):
+    def arm(T, n_seq, with_bias, per_sequence=False):
         U, us = [], []
         for l, (lw, _) in enumerate(layers):
             x, _, Wr = synth.layer_inputs(wl, l, T=T, n_seq=n_seq)
@@ -400,7 +458,9 @@ def config_ab(m, synth, wl, layers, dev, reps=15):
             bias = None
             if with_bias:
                 rng = synth.rng_for(0, wl.cid, 999)
-                bias = m.Bias(cap=2 * wl.k, alpha=0.5, w_conf=to_dev(rng.random(T).astype(np.float32)))
+                offsets = list(range(0, T + 1, T // n_seq)) if per_sequence else None
+                bias = m.Bias(cap=2 * wl.k, alpha=0.5, w_conf=to_dev(rng.random(T).astype(np.float32)),
+                              offsets=offsets)
             ws = m.alloc_workspace(lw2, T, bias, device=dev)
             y = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
             m.verify_layer(xd, lw2, bias, out=y, workspace=ws)
@@ -420,13 +480,16 @@ def config_ab(m, synth, wl, layers, dev, reps=15):
                 "verify_kernel_us_per_layer": round(float(np.mean(us)), 1), "unions": U}
 
     res = {"width_vs_depth_T2": {"depth_one_sequence": arm(2, 1, False), "width_two_sequences": arm(2, 2, False)},
-           "reuse_bias": {"off": arm(wl.T, wl.n_seq, False), "on": arm(wl.T, wl.n_seq, True)}}
+           "reuse_bias": {"off": arm(wl.T, wl.n_seq, False), "on": arm(wl.T, wl.n_seq, True),
+                          "on_per_sequence": arm(wl.T, wl.n_seq, True, per_sequence=True)}}
     wd, rb = res["width_vs_depth_T2"], res["reuse_bias"]
     err(f"[bench] T=2 depth: U {wd['depth_one_sequence']['unique_experts_per_layer']}, "
         f"{wd['depth_one_sequence']['verify_kernel_us_per_layer']} us; width: U "
         f"{wd['width_two_sequences']['unique_experts_per_layer']}, {wd['width_two_sequences']['verify_kernel_us_per_layer']} us")
     err(f"[bench] bias off: U {rb['off']['unique_experts_per_layer']}, {rb['off']['verify_kernel_us_per_layer']} us; "
-        f"on: U {rb['on']['unique_experts_per_layer']}, {rb['on']['verify_kernel_us_per_layer']} us")
+        f"on (pooled): U {rb['on']['unique_experts_per_layer']}, {rb['on']['verify_kernel_us_per_layer']} us; "
+        f"on (per sequence): U {rb['on_per_sequence']['unique_experts_per_layer']}, "
+        f"{rb['on_per_sequence']['verify_kernel_us_per_layer']} us")
     return res
 
 
@@ -464,19 +527,27 @@ def select_timing(m, synth, wl, dev, stream, nt=4096, reps=20):
             "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
-def cpu_baseline(wl, budget_s, U0, be, n_sh):
+def cpu_threads():
+    """Threads the CPU oracle may use: the process's CPU share
+    (OMP_NUM_THREADS when the environment sets it, else the CPUs this
+    process may run on)."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(env) if env.isdigit() and int(env) > 0 else len(os.sched_getaffinity(0))
+    return max(1, n)
+
+
+def cpu_baseline(wl, budget_s, be, n_sh):
     """The CPU oracle (plain NumPy, float64) on layer 0 of the same workload:
     router logits, routing, and the per-token dense loop over each token's
-    top-k experts.  Weight regeneration/decoding is outside the timing."""
+    top-k experts, with the BLAS thread pool set to the process's CPU share
+    and then to one thread.  Weight regeneration and decoding are outside the
+    timing."""
     import numpy as np
     import synth
     from oracle import fp as ofp
     from oracle import moe as omoe
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = cpu_threads()
     x, _, Wr = synth.layer_inputs(wl, 0)
     logits = omoe.router_logits(x, Wr).astype(np.float32)
     r = omoe.route(logits, wl.k)
@@ -491,46 +562,48 @@ def cpu_baseline(wl, budget_s, U0, be, n_sh):
         cache[int(e)] = (gu[:wl.I], gu[wl.I:], d)
     t_regen = time.perf_counter() - t_regen
     shared = cache[wl.E] if wl.shared else None
-    reps, t_total = 0, 0.0
-    while t_total < budget_s or reps == 0:
-        t = time.perf_counter()
+    U = len(omoe.expert_union(r.topk_idx))
+
+    def one_layer():
         lg = omoe.router_logits(x, Wr).astype(np.float32)
         rr = omoe.route(lg, wl.k)
         omoe.moe_layer(x, rr.topk_idx, rr.topk_w, lambda e: cache[e], shared=shared)
-        t_total += time.perf_counter() - t
-        reps += 1
-    per_layer = t_total / reps
-    U = len(omoe.expert_union(r.topk_idx))
-    gbs = (U + n_sh) * be / per_layer / 1e9
-    err(f"[bench] cpu oracle: {per_layer * 1e3:.1f} ms/layer ({reps} reps), {gbs:.2f} GB/s, {threads} threads")
-    # the same on one thread, one repetition
-    single = None
-    try:
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
+
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        reps, t_total = 0, 0.0
+        while t_total < budget_s or reps == 0:
             t = time.perf_counter()
-            lg = omoe.router_logits(x, Wr).astype(np.float32)
-            rr = omoe.route(lg, wl.k)
-            omoe.moe_layer(x, rr.topk_idx, rr.topk_w, lambda e: cache[e], shared=shared)
-            t1 = time.perf_counter() - t
-        single = {"value": round((U + n_sh) * be / t1 / 1e9, 3), "ms_per_layer": round(t1 * 1e3, 1)}
-        err(f"[bench] cpu oracle, 1 thread: {t1 * 1e3:.1f} ms/layer")
-    except Exception:
-        pass
+            one_layer()
+            t_total += time.perf_counter() - t
+            reps += 1
+    per_layer = t_total / reps
+    gbs = (U + n_sh) * be / per_layer / 1e9
+    err(f"[bench] cpu oracle: {per_layer * 1e3:.1f} ms/layer ({reps} reps), {gbs:.2f} GB/s, {used} threads")
+    # the same on one thread
+    with threadpool_limits(limits=1):
+        reps1, t1 = 0, 0.0
+        while t1 < budget_s / 4 or reps1 == 0:
+            t = time.perf_counter()
+            one_layer()
+            t1 += time.perf_counter() - t
+            reps1 += 1
+    t1 /= reps1
+    single = {"value": round((U + n_sh) * be / t1 / 1e9, 3), "ms_per_layer": round(t1 * 1e3, 1), "reps": reps1}
+    err(f"[bench] cpu oracle, 1 thread: {t1 * 1e3:.1f} ms/layer")
     # the selection oracle ([EcoSpec] section 3.3) per batch of 16 trees
     from oracle import select as osel
     trees = synth.draft_trees(seed=5, nt=16, n_layers=MODEL_LAYERS[wl.name], E=wl.E, k=wl.k)
     t = time.perf_counter()
     osel.select_drafts_batch(trees.P, trees.F, 4)
     sel_ms = (time.perf_counter() - t) * 1e3
-    out = {"value": round(gbs, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-           "sample": f"layer 0 of {wl.name} (union {U} experts), {reps} repetitions of router logits + "
-                     f"routing + per-token dense float64 loop; {per_layer * 1e3:.1f} ms/layer; expert "
-                     f"regeneration and decoding ({t_regen:.1f} s) untimed",
-           "select_ms_per_16_trees": round(sel_ms, 2)}
-    if single is not None:
-        out["single_thread"] = single
-    return out
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": int(used), "kind": "oracle",
+            "sample": f"layer 0 of {wl.name} (union {U} experts{' + shared' if n_sh else ''}), {reps} repetitions "
+                      f"of router logits + routing + per-token dense float64 loop; {per_layer * 1e3:.1f} ms/layer; "
+                      f"expert regeneration and decoding ({t_regen:.1f} s) untimed",
+            "ms_per_layer": round(per_layer * 1e3, 1), "os_cpu_count": os.cpu_count(),
+            "threads_note": "BLAS threads = the process's CPU share (OMP_NUM_THREADS, else its CPU affinity)",
+            "single_thread": single, "select_ms_per_16_trees": round(sel_ms, 2)}
 
 
 if __name__ == "__main__":
