@@ -193,6 +193,24 @@ size_t moe_verify_workspace_bytes(const moe_layer *layer, int32_t T, const moe_b
 int moe_verify_layer(const moe_layer *layer, const float *x, int32_t T, const moe_bias *bias,
                      float *y, moe_aux *aux, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_verify_layer for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors as moe_verify_layer,
+ * without the workspace: the call uses a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes, one per GPU the library runs on, held
+ * until the process ends.  It allocates nothing (no hipMalloc, no allocating
+ * library routine).  Every call on a GPU shares that GPU's array and leaves
+ * it holding that call's workspace; calls that overlap on one GPU (other
+ * streams, other threads) race on it and give undefined results, so
+ * serialise them.  A call whose workspace (moe_verify_workspace_bytes)
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_EWORKSPACE before anything
+ * is enqueued.  The first call on each device looks up the array's device
+ * address (hipGetSymbolAddress) and keeps it; make that call outside stream
+ * capture. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_verify_layer_noalloc(const moe_layer *layer, const float *x, int32_t T, const moe_bias *bias,
+                             float *y, moe_aux *aux, void *stream);
+
 /* Per-layer union statistics ([S2-MoE] motivation, challenge 2: reuse ratio
  * = number of distinct experts over s * k).  topk_idx [nL, T, k] int32
  * (device), entries in [0, E) (entries outside are ignored);

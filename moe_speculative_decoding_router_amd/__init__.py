@@ -8,6 +8,7 @@ not built, the first call raises; there is no fallback.
 Entry points (same names as the C ABI in include/moe_verify.h):
   pack_weights(src, wdtype, gate_up)  -> packed weights (one-time preparation)
   verify_layer(x, layer, bias=None)   -> (y, aux)
+  verify_layer_noalloc(x, layer, bias=None, out=None, aux=None) -> (y, aux)
   union_stats(topk_idx, E)            -> (counts, reuse)
   select_drafts(parent, P, Epred, gamma, eps=1e-6, static=False) -> S
   expand_drafts(parent, P, Epred, t_ar, t_exp, c_draft=None) -> (S, count)
@@ -34,7 +35,7 @@ MAX_SEGMENTS = 64
 STAGE_NAMES = ("router", "route", "gate_up", "down", "combine")
 EXPORTED = ("moe_pack_weights", "moe_verify_workspace_bytes", "moe_verify_layer", "union_stats",
             "select_drafts", "select_drafts_static", "expand_drafts", "union_stats_segments", "gate_depths",
-            "moe_stream_read", "moe_last_error")
+            "moe_stream_read", "moe_last_error", "moe_verify_layer_noalloc")
 
 _vp, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 
@@ -71,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.moe_verify_layer.argtypes = [ctypes.POINTER(_Layer), _vp, _i32, ctypes.POINTER(_Bias), _vp,
                                        ctypes.POINTER(_Aux), _vp, ctypes.c_size_t, _vp]
         L.moe_verify_layer.restype = ctypes.c_int
+        L.moe_verify_layer_noalloc.argtypes = [ctypes.POINTER(_Layer), _vp, _i32, ctypes.POINTER(_Bias), _vp,
+                                               ctypes.POINTER(_Aux), _vp]
+        L.moe_verify_layer_noalloc.restype = ctypes.c_int
         L.union_stats.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
         L.union_stats.restype = ctypes.c_int
         L.select_drafts.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _f32, _i32, _vp, _vp]
@@ -462,6 +466,40 @@ def verify_layer(x, layer: LayerWeights, bias: Optional[Bias] = None, *, out=Non
                                 ctypes.byref(caux), workspace.ws.data_ptr(), workspace.nbytes, s)
     _check(rc)
     return y, a
+
+
+def verify_layer_noalloc(x, layer: LayerWeights, bias: Optional[Bias] = None, *, out=None,
+                         aux: Optional[Aux] = None, stream=None):
+    """moe_verify_layer_noalloc: the verify call on the library's own per-GPU
+    workspace array, for callers that cannot allocate (`out` and `aux` given,
+    this call allocates nothing either).  Calls that overlap on one GPU race
+    on the shared array.  Returns (y, aux)."""
+    import torch
+    if not hasattr(x, "dim") or x.dim() != 2:
+        raise ValueError("x must be a contiguous float32 [T, H] tensor")
+    T = int(x.shape[0])
+    dev = x.device
+    _check_tensor(x, "x", ("float32",), shape=(T, layer.H))
+    if dev.type != "cuda":
+        raise ValueError(f"x must be a device tensor, got {dev}")
+    layer.validate(dev)
+    if bias is not None:
+        bias.check(T, dev)
+    if out is not None:
+        _check_tensor(out, "out", ("float32",), shape=(T, layer.H), device=dev)
+    if aux is not None:
+        for f, (n, dt) in _aux_sizes(layer, T, bias).items():
+            t = getattr(aux, f)
+            if t is not None:
+                _check_tensor(t, f"aux.{f}", dt, numel=n, device=dev, at_least=True)
+    y = out if out is not None else torch.empty_like(x)
+    L = layer._c()
+    b = bias._c() if bias is not None else None
+    caux = _Aux(*([_ptr(getattr(aux, f)) for f in Aux.__dataclass_fields__] if aux else [None] * 10), None)
+    s = _launch_stream(stream, dev, [y] if out is None else [])
+    _check(lib().moe_verify_layer_noalloc(ctypes.byref(L), x.data_ptr(), T, ctypes.byref(b) if b else None,
+                                          y.data_ptr(), ctypes.byref(caux), s))
+    return y, aux
 
 
 def union_stats(topk_idx, E: int, counts=None, reuse=None, stream=None):

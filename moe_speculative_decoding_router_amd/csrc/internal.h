@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_verify.h"
+
 namespace moe {
 
 constexpr int kMaxSegments = 64;  // sequences of one call (ragged verify, per-sequence bias)
@@ -116,6 +118,11 @@ hipError_t launch_segment_stats(const int32_t *topk_idx, int nL, int T, int k, i
 size_t gate_lds_bytes(int W);
 hipError_t launch_gate_depths(const float *c, const uint32_t *Ep, int S, int Dmax, int W, float t_base,
                               float t_exp, int32_t *d, hipStream_t s);
+
+// Host helpers of the C ABI (moe_verify.cpp): the error message of the
+// calling thread, and the validation plus workspace size of a verify call.
+int set_error(int code, const char *msg);
+int verify_needs(const ::moe_layer *layer, int T, const ::moe_bias *bias, size_t *need);
 
 // Limits used by the kernels.
 constexpr int kMaxTokens = 64;

@@ -164,6 +164,19 @@ int validate_layer(const moe_layer *L, int T, const moe_bias *bias) {
 
 }  // namespace
 
+namespace moe {
+
+int set_error(int code, const char *msg) { return fail(code, "%s", msg); }
+
+int verify_needs(const moe_layer *layer, int T, const moe_bias *bias, size_t *need) {
+    const int rc = validate_layer(layer, T, bias);
+    if (rc != MOE_OK) return rc;
+    *need = make_layout(*layer, T, bias).total;
+    return MOE_OK;
+}
+
+}  // namespace moe
+
 extern "C" {
 
 const char *moe_last_error(void) { return g_err; }

@@ -152,3 +152,15 @@ def test_stream_read_validation(lib):
     assert lib.moe_stream_read(addr, 0, ctypes.addressof(out), None) == -1
     assert lib.moe_stream_read(addr, 24, ctypes.addressof(out), None) == -1
     assert lib.moe_stream_read(addr + 4, 16, ctypes.addressof(out), None) == -1
+
+
+def test_noalloc_rejects_calls_beyond_its_array(lib):
+    # 513 slots x 4096 x 64 columns of hidden activations alone exceed the
+    # 32 MiB array: refused before anything touches a device
+    L = layer(H=512, I=4096, E=512, k=32)
+    assert ws_bytes(lib, L, 64) > (32 << 20)
+    rc = lib.moe_verify_layer_noalloc(ctypes.byref(L), 16, 64, None, 16, None, None)
+    assert rc == -3 and b"no-allocation" in lib.moe_last_error()
+    # invalid arguments keep their own codes
+    assert lib.moe_verify_layer_noalloc(ctypes.byref(layer(k=0)), 16, 5, None, 16, None, None) == -1
+    assert lib.moe_verify_layer_noalloc(None, 16, 5, None, 16, None, None) == -1
