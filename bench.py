@@ -316,6 +316,9 @@ def calibrate_cost_model(m, synth, wl, layers, dev, Ts=(1, 2, 3, 4, 5, 6, 8, 10,
                     "tokens of one sequence on each cycled layer, median of 5 calls"}
 
 
+ABLATION_SCATTER, ABLATION_RHO = 2.0, 0.8
+
+
 def ablation(m, synth, wl, layers, ML, dev, stream, n_trees=8, n_layers=8):
     """EcoSpec variants on synthetic trees ([EcoSpec] section 4.3): for
     gamma = 3..6 the drafts chosen by the marginal cost (select_drafts), by
@@ -323,11 +326,17 @@ def ablation(m, synth, wl, layers, ML, dev, stream, n_trees=8, n_layers=8):
     alone (the static selection with empty footprints: top-gamma by P) are
     verified together with the root token, each token routed to its own
     predicted experts (a perfect predictor), on n_layers of the model's
-    layers; reports the unique experts per layer (from the library) and the
-    verify kernel time per layer (router + gate-up + down events)."""
+    layers; reports the unique experts per layer (from the library), the
+    verify kernel time per layer (router + gate-up + down events) and the
+    expected accepted drafts (the sum of P over the chosen nodes, which is
+    the expectation for a prefix-closed choice).  The trees scatter their
+    branches over the experts ([EcoSpec] section 1: candidates close in
+    probability, far apart in expert space): synth.draft_trees with a path
+    context that follows each branch."""
     import numpy as np
     import torch
-    trees = synth.draft_trees(seed=11, nt=n_trees, n_layers=ML, E=wl.E, k=wl.k, rate=wl.rate, with_own=True)
+    trees = synth.draft_trees(seed=11, nt=n_trees, n_layers=ML, E=wl.E, k=wl.k, rate=wl.rate, with_own=True,
+                              branch_scatter=ABLATION_SCATTER, branch_rho=ABLATION_RHO)
     P_d = torch.from_numpy(trees.P).to(dev)
     F_d = torch.from_numpy(trees.F.view(np.int32)).to(dev)
     Z_d = torch.zeros_like(F_d)
@@ -338,15 +347,18 @@ def ablation(m, synth, wl, layers, ML, dev, stream, n_trees=8, n_layers=8):
         e.record(stream)
     torch.cuda.synchronize()
     res = {"gamma": [3, 4, 5, 6], "trees": n_trees, "layers": n_layers,
-           "note": "tokens routed to their predicted experts; unique experts and kernel us per layer"}
+           "branch_scatter": ABLATION_SCATTER, "branch_rho": ABLATION_RHO,
+           "note": "tokens routed to their predicted experts; unique experts and kernel us per layer; "
+                   "expected accepted drafts = sum of P over the chosen nodes"}
     for mode in ("marginal", "static", "confidence"):
-        U_m, us_m = [], []
+        U_m, us_m, acc_m = [], [], []
         for gamma in res["gamma"]:
             if mode == "marginal":
                 S = m.select_drafts(trees.parent, P_d, F_d, gamma)
             else:
                 S = m.select_drafts(trees.parent, P_d, F_d if mode == "static" else Z_d, gamma, static=True)
             S = S.cpu().numpy()
+            acc_m.append(round(float(np.mean([trees.P[t][S[t]].sum() for t in range(n_trees)])), 3))
             us, uu = [], []
             for t in range(n_trees):
                 sets = np.concatenate([trees.root_own[t][None], trees.own[t][S[t]]], axis=0)
@@ -367,8 +379,9 @@ def ablation(m, synth, wl, layers, ML, dev, stream, n_trees=8, n_layers=8):
                     uu.append(int(wsp.aux.union_size.item()))
             U_m.append(round(float(np.mean(uu)), 2))
             us_m.append(round(float(np.mean(us)), 1))
-        res[mode] = {"unique_experts_per_layer": U_m, "verify_kernel_us_per_layer": us_m}
-        err(f"[bench] ablation {mode}: U {U_m} us {us_m}")
+        res[mode] = {"unique_experts_per_layer": U_m, "verify_kernel_us_per_layer": us_m,
+                     "expected_accepted_drafts": acc_m}
+        err(f"[bench] ablation {mode}: U {U_m} us {us_m} accepted {acc_m}")
     return res
 
 

@@ -306,7 +306,8 @@ def tree_parents(depth: int, branch: int) -> np.ndarray:
 
 def draft_trees(seed: int, nt: int, depth: int = 3, branch: int = 2, n_layers: int = 36,
                 E: int = 128, k: int = 4, rate: float = 0.05, p_lo: float = 0.3,
-                stream: int = 0, chunk: int = 256, with_own: bool = False) -> DraftTrees:
+                stream: int = 0, chunk: int = 256, with_own: bool = False,
+                branch_scatter: float = 0.0, branch_rho: float = 0.5) -> DraftTrees:
     """Batch of nt draft trees.
 
     Each node draws its own per-layer set of k distinct experts, sampled
@@ -317,7 +318,15 @@ def draft_trees(seed: int, nt: int, depth: int = 3, branch: int = 2, n_layers: i
     Edge probabilities are U(p_lo, 1); P is their running product in
     float32 (so P(child) <= P(parent)).  with_own also returns each node's
     own sets and a root token's sets (same model and tree context, drawn from
-    a separate stream, so the trees themselves do not change)."""
+    a separate stream, so the trees themselves do not change).
+
+    branch_scatter > 0 adds branch_scatter * b_i to every node's weights,
+    where b_i is a path context that follows the tree: b_i = z_i for a child
+    of the root and b_i = rho b_parent + sqrt(1 - rho^2) z_i below it, with
+    z_i ~ N(0, 1) per (node, layer, expert).  Siblings then route apart
+    while a child stays close to its parent: draft candidates that are close
+    in probability but spread over the experts.  Its draws come from a
+    stream of their own, so the trees without it do not change."""
     parent = tree_parents(depth, branch)
     N = len(parent)
     W = (n_layers * E + 31) // 32
@@ -326,6 +335,7 @@ def draft_trees(seed: int, nt: int, depth: int = 3, branch: int = 2, n_layers: i
     OWN = np.zeros((nt, N, W), dtype=np.uint32) if with_own else None
     ROOT = np.zeros((nt, W), dtype=np.uint32) if with_own else None
     rng_root = rng_for(seed, 3, stream, 1) if with_own else None
+    rng_branch = rng_for(seed, 3, stream, 2) if branch_scatter > 0 else None
     rng = rng_for(seed, 3, stream)
     rank = rng.permutation(E).astype(np.float64)
     pop = 1.5 * np.exp(-rate * rank)
@@ -335,6 +345,13 @@ def draft_trees(seed: int, nt: int, depth: int = 3, branch: int = 2, n_layers: i
         noise = 0.7 * rng.standard_normal((c, N, n_layers, E))
         gumbel = -np.log(-np.log(rng.uniform(1e-300, 1.0, size=(c, N, n_layers, E))))
         keys = pop + ctx + noise + gumbel
+        if branch_scatter > 0:
+            z = rng_branch.standard_normal((c, N, n_layers, E))
+            b = np.zeros_like(z)
+            for i in range(N):
+                pi = parent[i]
+                b[:, i] = z[:, i] if pi < 0 else branch_rho * b[:, pi] + math.sqrt(1.0 - branch_rho ** 2) * z[:, i]
+            keys = keys + branch_scatter * b
         sel = np.argpartition(-keys, k - 1, axis=-1)[..., :k]
         own = np.zeros((c, N, n_layers, E), dtype=bool)
         np.put_along_axis(own, sel, True, axis=-1)

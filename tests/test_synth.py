@@ -104,3 +104,26 @@ def test_tree_own_sets_and_logits_for_sets():
             top = np.argsort(-lg, axis=1)[:, :2]
             for r in range(sets.shape[0]):
                 assert set(top[r].tolist()) == set(np.nonzero(per_layer(sets[r])[layer])[0].tolist())
+
+
+def test_draft_trees_branch_scatter():
+    """With a path context per branch, a child routes close to its parent and
+    siblings route apart; without it the trees are the same as before."""
+    a = synth.draft_trees(seed=3, nt=8, n_layers=6, E=64, k=4, with_own=True)
+    b = synth.draft_trees(seed=3, nt=8, n_layers=6, E=64, k=4, with_own=True, branch_scatter=0.0)
+    assert np.array_equal(a.F, b.F) and np.array_equal(a.P, b.P) and np.array_equal(a.own, b.own)
+    def parent_vs_sibling(tr):
+        own = np.unpackbits(tr.own.view(np.uint8), axis=-1, bitorder="little").astype(bool)
+
+        def overlap(i, j):
+            return float((own[:, i] & own[:, j]).sum(axis=-1).mean())
+        par = tr.parent
+        pc = np.mean([overlap(i, par[i]) for i in range(len(par)) if par[i] >= 0])
+        sib = np.mean([overlap(i, i + 1) for i in range(0, len(par), 2)])
+        return pc / sib
+
+    plain = synth.draft_trees(seed=3, nt=64, n_layers=6, E=64, k=4, with_own=True)
+    scat = synth.draft_trees(seed=3, nt=64, n_layers=6, E=64, k=4, with_own=True, branch_scatter=2.0, branch_rho=0.8)
+    assert np.array_equal(scat.P, plain.P)           # the probabilities are drawn as before
+    assert 0.9 < parent_vs_sibling(plain) < 1.1      # one context per tree: no branch structure
+    assert parent_vs_sibling(scat) > 1.2
