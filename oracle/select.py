@@ -45,32 +45,41 @@ def score(P_t, c: int, eps: float) -> np.float32:
     return np.float32(np.float32(P_t) / (np.float32(c) + np.float32(eps)))
 
 
+def popcounts(words: np.ndarray) -> np.ndarray:
+    """Number of set bits of each row of a [..., W] uint32 bitset array."""
+    w = np.ascontiguousarray(np.asarray(words, dtype=np.uint32))
+    return np.unpackbits(w.view(np.uint8), axis=-1).sum(axis=-1).astype(np.int64)
+
+
 def select_drafts(P: np.ndarray, F: np.ndarray, gamma: int, eps: float = 1e-6, static: bool = False) -> List[int]:
-    """Greedy cost-aware selection for one tree; returns node ids in pick order.
+    """Cost-aware selection for one tree; returns node ids in pick order.
 
     P: [N] float32 path probabilities; F: [N, W] uint32 path footprints.
-    static: the ablation of [EcoSpec] section 4.3, where the cost is the size
-    of the whole path footprint and is not updated by the selection (the
-    buffer B stays empty)."""
+    Each round scores every node at once, S = P / (|F \\ B| + eps) in
+    float32 (§3.3), with the nodes already taken scored -inf, and takes the
+    first node in (score desc, index asc) order; its footprint then joins
+    the buffer B, which starts empty (§3.2).  static: the ablation of
+    [EcoSpec] section 4.3, where the cost is the size of the whole path
+    footprint (B stays empty)."""
     P = np.asarray(P, dtype=np.float32)
     F = np.asarray(F, dtype=np.uint32)
     N = P.shape[0]
     if not 0 <= gamma <= N:
         raise ValueError("need 0 <= gamma <= N")
     B = np.zeros(F.shape[1], dtype=np.uint32)
-    chosen: List[int] = []
+    taken = np.zeros(N, dtype=bool)
+    picks: List[int] = []
+    node = np.arange(N)
     for _ in range(gamma):
-        best, best_s = -1, None
-        for t in range(N):
-            if t in chosen:
-                continue
-            s = score(P[t], new_pairs(F[t], B), eps)
-            if best_s is None or s > best_s:      # strict: ties keep the lower index
-                best, best_s = t, s
-        chosen.append(best)
+        cost = popcounts(F & ~B[None, :]).astype(np.float32)          # new (layer, expert) pairs
+        score = P / (cost + np.float32(eps))                             # two float32 operations
+        score = np.where(taken, np.float32(-np.inf), score)
+        pick = int(np.lexsort((node, -score))[0])                        # score desc, then index asc
+        picks.append(pick)
+        taken[pick] = True
         if not static:
-            B |= F[best]
-    return chosen
+            B = B | F[pick]
+    return picks
 
 
 def select_drafts_batch(P: np.ndarray, F: np.ndarray, gamma: int, eps: float = 1e-6,
