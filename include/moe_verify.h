@@ -232,8 +232,9 @@ int union_stats(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32
  * divide, each correctly rounded), choose the highest score (ties: lowest
  * node index), B |= F_chosen.  S [nt, gamma] int32 receives node ids in
  * choice order.  P, Epred and S may be NULL when gamma == 0 or nt == 0.
- * Limits: 0 <= gamma <= N <= 4096, 1 <= W <= 4096, N * W + W + N + N / 32 <= 16384
- * (the tree is staged in 64 KB of LDS), eps > 0. */
+ * Limits: 0 <= gamma <= N <= 4096, 1 <= W <= 4096, eps > 0.  A tree whose
+ * footprints fit in 64 KB of LDS (N * W + W + N + N / 32 <= 16384 words) is
+ * staged there once; a larger one is read from global memory every round. */
 int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred,
                   int32_t W, int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream);
 
@@ -294,8 +295,9 @@ int select_drafts_static(const int32_t *parent, int32_t N, const float *P, const
  *   c_draft [nt, N] float32 draft-side cost of each node, or NULL (zero)
  *   S       [nt, N] int32 out: nodes in the order they join, then -1
  *   count   [nt] int32 out: size of each set
- * Limits: N <= 1024 and N * W + W + 3 N + N / 32 <= 16384 words (LDS stage).
- * Errors: EINVAL (NULL, shapes, parent order, t_ar / t_exp), ENOTSUP (LDS). */
+ * Limits: N <= 1024, W <= 4096.  Footprints are staged in LDS when
+ * N * W + W + 3 N + N / 32 <= 16384 words, else read from global memory.
+ * Errors: EINVAL (NULL, shapes, parent order, t_ar / t_exp). */
 int expand_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred, int32_t W,
                   float t_ar, float t_exp, const float *c_draft, int32_t nt, int32_t *S, int32_t *count,
                   void *stream);

@@ -101,7 +101,7 @@ struct ExpandArgs {
     float t_ar, t_exp;
     int16_t parent[kMaxExpandNodes];
 };
-size_t expand_lds_bytes(int N, int W);
+size_t expand_lds_bytes(int N, int W, bool staged);
 hipError_t launch_expand(ExpandArgs a, const float *P, const uint32_t *F, const float *Cd, int32_t *S,
                          int32_t *count, hipStream_t s);
 

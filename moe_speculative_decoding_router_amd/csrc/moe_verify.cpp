@@ -338,9 +338,6 @@ static int select_common(const int32_t *parent, int32_t N, const float *P, const
     for (int i = 0; i < N; ++i)
         if (parent[i] < -1 || parent[i] >= i)
             return fail(MOE_EINVAL, "parent[%d]=%d: nodes must be in BFS order (parent < child)", i, parent[i]);
-    if ((size_t)N * W + W + N + (N + 31) / 32 > (size_t)moe::kSelectMaxLdsWords)
-        return fail(MOE_ENOTSUP, "tree footprint of %d x %d words exceeds the %d-word LDS stage", N, W,
-                    moe::kSelectMaxLdsWords);
     if (nt == 0 || gamma == 0) return MOE_OK;  // nothing to write
     if (!P || !Epred || !S) return fail(MOE_EINVAL, "NULL pointer");
     hipError_t err = moe::launch_select(N, P, Epred, W, gamma, eps, nt, S, update_b, static_cast<hipStream_t>(stream));
@@ -373,8 +370,8 @@ int expand_drafts(const int32_t *parent, int32_t N, const float *P, const uint32
             return fail(MOE_EINVAL, "parent[%d]=%d: nodes must be in BFS order (parent < child)", i, parent[i]);
         a.parent[i] = (int16_t)parent[i];
     }
-    if (moe::expand_lds_bytes(N, W) > (size_t)moe::kSelectMaxLdsWords * 4)
-        return fail(MOE_ENOTSUP, "tree footprint of %d x %d words exceeds the %d-word LDS stage", N, W,
+    if (moe::expand_lds_bytes(N, W, false) > (size_t)moe::kSelectMaxLdsWords * 4)
+        return fail(MOE_ENOTSUP, "tree of %d nodes x %d words needs more than %d words of LDS state", N, W,
                     moe::kSelectMaxLdsWords);
     if (nt == 0) return MOE_OK;
     if (!P || !Epred || !S || !count) return fail(MOE_EINVAL, "NULL pointer");

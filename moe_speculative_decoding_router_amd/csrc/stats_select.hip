@@ -50,26 +50,31 @@ __global__ __launch_bounds__(256) void union_stats_kernel(const int32_t *__restr
 // every node pays its whole footprint).
 constexpr int kSelThreads = 256;
 
+// STAGED: the tree's footprints are copied into LDS once; otherwise (a tree
+// larger than the LDS stage) every round reads them from global memory, where
+// after the first round they are L2 hits.
+template <bool STAGED>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(int N, const float *__restrict__ P,
                                                              const uint32_t *__restrict__ F, int W, int gamma,
                                                              float eps, int nt, int tpn, int update_b, int32_t *S) {
     extern __shared__ uint32_t lds[];
-    uint32_t *Fs = lds;                                   // [N * W]
-    uint32_t *Bs = Fs + (size_t)N * W;                    // [W]
-    float *sc = reinterpret_cast<float *>(Bs + W);        // [N]
-    uint32_t *chosen = reinterpret_cast<uint32_t *>(sc + N);  // [ceil(N / 32)]
-    __shared__ int best_sh;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int tree = blockIdx.x;
     if (tree >= nt) return;
     const uint32_t *Ft = F + (size_t)tree * N * W;
+    const uint32_t *Fs = STAGED ? lds : Ft;                                   // [N * W]
+    uint32_t *Bs = lds + (STAGED ? (size_t)N * W : 0);                        // [W]
+    float *sc = reinterpret_cast<float *>(Bs + W);        // [N]
+    uint32_t *chosen = reinterpret_cast<uint32_t *>(sc + N);  // [ceil(N / 32)]
+    __shared__ int best_sh;
     const float *Pt = P + (size_t)tree * N;
     const int nwords = N * W;
-    if (((nwords & 3) == 0) && ((reinterpret_cast<uintptr_t>(Ft) & 15) == 0)) {
+    if (!STAGED) {
+    } else if (((nwords & 3) == 0) && ((reinterpret_cast<uintptr_t>(Ft) & 15) == 0)) {
         // every load of a thread is issued before its LDS stores (one round trip)
         constexpr int kPer = kSelectMaxLdsWords / 4 / kSelThreads;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(Ft);
-        u32x4 *dst = reinterpret_cast<u32x4 *>(Fs);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(lds);
         const int n4 = nwords / 4;
         u32x4 v[kPer];
 #pragma unroll
@@ -78,7 +83,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int N, const float 
         for (int r = 0; r < kPer; ++r)
             if (tid + r * kSelThreads < n4) dst[tid + r * kSelThreads] = v[r];
     } else {
-        for (int i = tid; i < nwords; i += kSelThreads) Fs[i] = Ft[i];
+        for (int i = tid; i < nwords; i += kSelThreads) lds[i] = Ft[i];
     }
     for (int i = tid; i < W; i += kSelThreads) Bs[i] = 0u;
     for (int i = tid; i < (N + 31) / 32; i += kSelThreads) chosen[i] = 0u;
@@ -137,24 +142,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int N, const float 
 // added to B.  When no node from the scan position passes, a new pass starts
 // from node 0 if the last pass added a node, else the tree is done: at most
 // 2 N + 1 rounds, and every wave sees the same decision.
+template <bool STAGED>
 __global__ __launch_bounds__(kSelThreads) void expand_kernel(ExpandArgs a, const float *__restrict__ P,
                                                              const uint32_t *__restrict__ F,
                                                              const float *__restrict__ Cd, int32_t *S,
                                                              int32_t *count) {
     extern __shared__ uint32_t lds[];
     const int N = a.N, W = a.W;
-    uint32_t *Fs = lds;                                          // [N * W]
-    uint32_t *Bs = Fs + (size_t)N * W;                           // [W]
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tree = blockIdx.x;
+    if (tree >= a.nt) return;
+    const uint32_t *Ft = F + (size_t)tree * N * W;
+    const uint32_t *Fs = STAGED ? lds : Ft;                      // [N * W]
+    uint32_t *Bs = lds + (STAGED ? (size_t)N * W : 0);           // [W]
     float *Ps = reinterpret_cast<float *>(Bs + W);               // [N]
     float *Cs = Ps + N;                                          // [N]
     int *cnt = reinterpret_cast<int *>(Cs + N);                  // [N]
     uint32_t *inS = reinterpret_cast<uint32_t *>(cnt + N);       // [ceil(N / 32)]
     __shared__ int pick_sh;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int tree = blockIdx.x;
-    if (tree >= a.nt) return;
-    const uint32_t *Ft = F + (size_t)tree * N * W;
-    for (int i = tid; i < N * W; i += kSelThreads) Fs[i] = Ft[i];
+    if (STAGED)
+        for (int i = tid; i < N * W; i += kSelThreads) lds[i] = Ft[i];
     for (int i = tid; i < W; i += kSelThreads) Bs[i] = 0u;
     for (int i = tid; i < N; i += kSelThreads) {
         Ps[i] = P[(size_t)tree * N + i];
@@ -231,26 +238,40 @@ hipError_t launch_union_stats(const int32_t *topk_idx, int nL, int T, int k, int
     return hipGetLastError();
 }
 
-size_t expand_lds_bytes(int N, int W) { return ((size_t)N * W + W + 3 * (size_t)N + (N + 31) / 32) * 4; }
+size_t expand_lds_bytes(int N, int W, bool staged) {
+    return ((staged ? (size_t)N * W : 0) + W + 3 * (size_t)N + (N + 31) / 32) * 4;
+}
 
 hipError_t launch_expand(ExpandArgs a, const float *P, const uint32_t *F, const float *Cd, int32_t *S,
                          int32_t *count, hipStream_t s) {
     int tpn = 1;
     while (tpn * 2 <= 64 && tpn * 2 * a.N <= kSelThreads) tpn *= 2;
     a.tpn = tpn;
-    hipLaunchKernelGGL(expand_kernel, dim3(a.nt), dim3(kSelThreads), expand_lds_bytes(a.N, a.W), s, a, P, F, Cd,
-                       S, count);
+    const bool staged = expand_lds_bytes(a.N, a.W, true) <= (size_t)kSelectMaxLdsWords * 4;
+    if (staged)
+        hipLaunchKernelGGL(expand_kernel<true>, dim3(a.nt), dim3(kSelThreads), expand_lds_bytes(a.N, a.W, true), s,
+                           a, P, F, Cd, S, count);
+    else
+        hipLaunchKernelGGL(expand_kernel<false>, dim3(a.nt), dim3(kSelThreads), expand_lds_bytes(a.N, a.W, false),
+                           s, a, P, F, Cd, S, count);
     return hipGetLastError();
+}
+
+size_t select_lds_bytes(int N, int W, bool staged) {
+    return ((staged ? (size_t)N * W : 0) + W + N + (N + 31) / 32) * 4;
 }
 
 hipError_t launch_select(int N, const float *P, const uint32_t *F, int W, int gamma, float eps, int nt,
                          int32_t *S, bool update_b, hipStream_t s) {
-    const size_t lds = ((size_t)N * W + W + N + (N + 31) / 32) * 4;
     // threads per node: the largest power of two <= min(64, 256 / N), at least 1
     int tpn = 1;
     while (tpn * 2 <= 64 && tpn * 2 * N <= kSelThreads) tpn *= 2;
-    hipLaunchKernelGGL(select_kernel, dim3(nt), dim3(kSelThreads), lds, s, N, P, F, W, gamma, eps, nt, tpn,
-                       update_b ? 1 : 0, S);
+    if (select_lds_bytes(N, W, true) <= (size_t)kSelectMaxLdsWords * 4)
+        hipLaunchKernelGGL(select_kernel<true>, dim3(nt), dim3(kSelThreads), select_lds_bytes(N, W, true), s, N, P,
+                           F, W, gamma, eps, nt, tpn, update_b ? 1 : 0, S);
+    else
+        hipLaunchKernelGGL(select_kernel<false>, dim3(nt), dim3(kSelThreads), select_lds_bytes(N, W, false), s, N,
+                           P, F, W, gamma, eps, nt, tpn, update_b ? 1 : 0, S);
     return hipGetLastError();
 }
 

@@ -93,7 +93,10 @@ def test_union_stats_and_select_validation(lib):
     assert b"BFS" in lib.moe_last_error()
     assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4, 7, 1e-6, 1, 16, None) == -1   # gamma > N
     assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4, 4, 0.0, 1, 16, None) == -1    # eps <= 0
-    assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4000, 4, 1e-6, 1, 16, None) == -2  # LDS stage
+    # a tree larger than the LDS stage is accepted (read from global memory);
+    # nt = 0 keeps the check host-only
+    assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4000, 4, 1e-6, 0, 16, None) == 0
+    assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4097, 4, 1e-6, 0, 16, None) == -1  # W > 4096
     assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4, 0, 1e-6, 1, 16, None) == 0    # gamma 0
     assert lib.select_drafts(par.ctypes.data, 6, 16, 16, 4, 4, 1e-6, 0, 16, None) == 0    # no trees
 
@@ -107,7 +110,8 @@ def test_expand_validation(lib):
     assert b"BFS" in lib.moe_last_error()
     assert ok(par.ctypes.data, 6, 16, 16, 4, -1.0, 1.0, None, 1, 16, 16, None) == -1   # t_ar < 0
     assert ok(par.ctypes.data, 6, 16, 16, 4, 1.0, float("inf"), None, 1, 16, 16, None) == -1
-    assert ok(par.ctypes.data, 6, 16, 16, 4000, 1.0, 1.0, None, 1, 16, 16, None) == -2  # LDS stage
+    assert ok(par.ctypes.data, 6, 16, 16, 4000, 1.0, 1.0, None, 0, 16, 16, None) == 0   # beyond LDS: accepted
+    assert ok(par.ctypes.data, 6, 16, 16, 4097, 1.0, 1.0, None, 0, 16, 16, None) == -1  # W > 4096
     assert ok(par.ctypes.data, 6, None, 16, 4, 1.0, 1.0, None, 1, 16, 16, None) == -1   # P NULL
     assert ok(par.ctypes.data, 6, None, None, 4, 1.0, 1.0, None, 0, None, None, None) == 0  # no trees
     big = np.full(1025, -1, dtype=np.int32)

@@ -144,6 +144,34 @@ def test_random_trees(seed):
     assert np.array_equal(cnt.cpu().numpy(), (ref >= 0).sum(axis=1))
 
 
+@pytest.mark.parametrize("depth,branch,static", [(5, 2, False), (5, 2, True), (3, 4, False)])
+def test_select_trees_beyond_the_lds_stage(depth, branch, static):
+    """Trees whose full-model footprints exceed the 64 KB LDS stage (62 or 84
+    nodes x 376 words, Qwen3-shaped: 94 layers x 128 experts) are read from
+    global memory every round: select_drafts, its static-cost ablation and
+    expand_drafts bit for bit against the oracle, and the choice is
+    prefix-closed."""
+    trees = synth.draft_trees(seed=21, nt=24, depth=depth, branch=branch, n_layers=94, E=128, k=8)
+    nt, N, W = trees.F.shape
+    assert N * W + W + N + N // 32 > 16384
+    log(f"case select beyond LDS: N={N} W={W} static={static}")
+    Pd, Fd = to_dev(trees.P), to_dev(trees.F.view(np.int32))
+    S = m.select_drafts(trees.parent, Pd, Fd, 6, static=static)
+    torch.cuda.synchronize()
+    S = S.cpu().numpy()
+    assert np.array_equal(S, osel.select_drafts_batch(trees.P, trees.F, 6, static=static))
+    if not static:
+        for row in S:
+            chosen = set(row.tolist())
+            assert all(trees.parent[t] < 0 or trees.parent[t] in chosen for t in chosen)
+        E_cnt, t_ar = 8 * 94, 30.0
+        S2, cnt = m.expand_drafts(trees.parent, Pd, Fd, t_ar, t_ar / (2 * E_cnt))
+        torch.cuda.synchronize()
+        ref = oexp.expand_batch(trees.parent, trees.P, trees.F, t_ar, t_ar / (2 * E_cnt), np.zeros_like(trees.P))
+        assert np.array_equal(S2.cpu().numpy(), ref)
+        assert np.array_equal(cnt.cpu().numpy(), (ref >= 0).sum(axis=1))
+
+
 def chains(seed, S, Dmax, n_layers, E, k):
     """S sequences of Dmax chained drafts: cumulative confidences and the
     expert bitsets of each sequence's root and drafts."""
