@@ -324,14 +324,15 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
 
     int nslots;
     if (FUSED) {
-        // the waves without a token in the routing's first pass issue the
-        // chunks that do not overlap the routing scratch
-        if (early > 0) {
-            if (T < kGuWaves)
-                stage_x(T, kGuWaves - T, 0, early);
-            else
-                stage_x(0, kGuWaves, 0, early);
-        }
+        // The chunks that do not overlap the routing scratch are issued by
+        // the waves without a token in the routing's first pass, before it;
+        // when every wave has tokens, by all waves right after the per-token
+        // selections (issued earlier, they would queue ahead of the router
+        // logits that the selections wait for).
+        if (early > 0 && T < kGuWaves) stage_x(T, kGuWaves - T, 0, early);
+        auto after_pass1 = [&]() {
+            if (early > 0 && T >= kGuWaves) stage_x(0, kGuWaves, 0, early);
+        };
         // An always-on shared expert is slot 0, so this workgroup's first
         // item is its row tile b (while b < rtiles) whatever the routing
         // gives: the waves without a token pull the first half of that
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
             for (int c = w - T; c < nkt / 2; c += kGuWaves - T) load_lds16(sht + (size_t)c * 1024, &red[0][w][0][0]);
         }
         // routing, recomputed by every workgroup (bit-identical results)
-        block_route<kGuWaves * 64>(p, scr, sexp, nullptr, fin, &nslots_sh, blockIdx.x == 0);
+        block_route<kGuWaves * 64>(p, scr, sexp, nullptr, fin, &nslots_sh, blockIdx.x == 0, after_pass1);
         nslots = nslots_sh;
         if (early < nx) stage_x(0, kGuWaves, early, nx);
     } else {
@@ -368,15 +369,15 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     const int nb = (nbi + kGuWaves - 1) / kGuWaves;         // per wave per item
     // Items: workgroup b takes items b, b + G, ... up to its S0-th (G and b
     // counted among the workgroups of its contraction part).  When the
-    // operand is read from L2 (not held in LDS), the workgroups' streaming
-    // rates vary with L2 contention, and the remaining R items are handed
-    // out in order by a device-scope ticket counter, so the workgroups that
-    // stream faster take more of the tail.  A ticket is claimed three items
+    // operand is read from L2 (wholly, or for NGL units of every batch), the
+    // workgroups' streaming rates vary with L2 contention, and the remaining
+    // R items are handed out in order by a device-scope ticket counter, so
+    // the workgroups that stream faster take more of the tail.  A ticket is claimed three items
     // ahead of its use (right after the barrier of an item) and published to
     // LDS just before the barrier of the next item, which waits for every
     // outstanding load anyway.
     const int G = gridDim.x / KS, bid = blockIdx.x / KS;
-    const bool dyn = KS == 1 && !BLDS && p.gu_ticket != nullptr && items >= (kGuDynDepth + 3) * G;
+    const bool dyn = KS == 1 && (!BLDS || NGL > 0) && p.gu_ticket != nullptr && items >= (kGuDynDepth + 3) * G;
     const int S0 = dyn ? items / G - kGuDynDepth : 0;
     const int R = items - S0 * G;
     auto item_of = [&](int ord) -> int {

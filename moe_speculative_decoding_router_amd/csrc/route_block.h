@@ -304,9 +304,9 @@ struct RouteScratch {
 // before the call).  Barriers: pass 1, [bias: importance and preferred set
 // per sequence, re-selection], union scan, tables.
 // NJ: row entries per lane the selections scan (>= ceil(E / 64)).
-template <int NTHREADS, int NJ>
+template <int NTHREADS, int NJ, typename Hook>
 __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned char *scratch, int *sexp, float *tw,
-                                               int *fin, int *nslots_lds, bool write_global) {
+                                               int *fin, int *nslots_lds, bool write_global, const Hook &after_pass1) {
     static_assert(NTHREADS >= kMaxExperts, "the union scan gives every expert one thread");
     constexpr int NW = NTHREADS / 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -379,6 +379,7 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
         }
     }
     lds_barrier();
+    after_pass1();
 
     if (bias) {
         // ---- per sequence (the whole call when pooled, R16): importance
@@ -572,16 +573,23 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     lds_barrier();
 }
 
-// Routing with the selection loops sized for E.
-template <int NTHREADS>
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+// Routing with the selection loops sized for E.  after_pass1() runs in every
+// thread once the per-token selections are done (the caller's chance to
+// issue memory work that the remaining, LDS-only steps then overlap).
+template <int NTHREADS, typename Hook = NoHook>
 __device__ __forceinline__ void block_route(const VerifyParams &p, unsigned char *scratch, int *sexp, float *tw,
-                                            int *fin, int *nslots_lds, bool write_global) {
+                                            int *fin, int *nslots_lds, bool write_global,
+                                            const Hook &after_pass1 = Hook{}) {
     if (p.E <= 128)
-        block_route_nj<NTHREADS, 2>(p, scratch, sexp, tw, fin, nslots_lds, write_global);
+        block_route_nj<NTHREADS, 2>(p, scratch, sexp, tw, fin, nslots_lds, write_global, after_pass1);
     else if (p.E <= 256)
-        block_route_nj<NTHREADS, 4>(p, scratch, sexp, tw, fin, nslots_lds, write_global);
+        block_route_nj<NTHREADS, 4>(p, scratch, sexp, tw, fin, nslots_lds, write_global, after_pass1);
     else
-        block_route_nj<NTHREADS, kRouteNJ>(p, scratch, sexp, tw, fin, nslots_lds, write_global);
+        block_route_nj<NTHREADS, kRouteNJ>(p, scratch, sexp, tw, fin, nslots_lds, write_global, after_pass1);
 }
 
 }  // namespace moe
