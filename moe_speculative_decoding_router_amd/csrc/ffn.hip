@@ -35,6 +35,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "launch.h"
 #include "route_block.h"
 
 namespace moe {

@@ -1,7 +1,6 @@
 // Internal declarations shared by the HIP translation units of libmoeverify.
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,15 +65,6 @@ constexpr int kWaveSize = 64;
 struct KernelEvents {
     hipEvent_t start = nullptr, stop = nullptr;
 };
-
-template <typename F, typename... Args>
-hipError_t launch_k(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, KernelEvents ev, Args... args) {
-    if (ev.start || ev.stop)
-        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
-    else
-        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
-    return hipGetLastError();
-}
 
 hipError_t launch_router(const VerifyParams &p, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_route(const VerifyParams &p, hipStream_t s, KernelEvents ev = {});

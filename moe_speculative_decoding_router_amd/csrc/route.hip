@@ -10,6 +10,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "launch.h"
 #include "route_block.h"
 
 namespace moe {
