@@ -309,9 +309,12 @@ def calibrate_cost_model(m, synth, wl, layers, dev, Ts=(1, 2, 3, 4, 5, 6, 8, 10,
     mape = float(np.mean(np.abs(us - pred) / us))
     err(f"[bench] {wl.name}: cost model T_exp {b:.3f} us/expert, intercept {a:.2f} us, R2 {r2:.4f}, "
         f"MAPE {mape:.4f}, experts {int(u.min())}..{int(u.max())}")
+    t_arr = np.array(t_all)
+    per_T = [[int(T), round(float(u[t_arr == T].mean()), 2), round(float(us[t_arr == T].mean()), 1)] for T in Ts]
     return {"t_exp_us_per_unique_expert": round(float(b), 3), "intercept_us": round(float(a), 2),
             "r2": round(r2, 4), "mape": round(mape, 4), "points": len(us_all),
             "tokens": list(Ts), "experts_streamed_range": [int(u.min()), int(u.max())],
+            "per_T_experts_us": per_T,
             "note": "verify kernel time (router + gate-up + down) against experts streamed, T = 1..20 "
                     "tokens of one sequence on each cycled layer, median of 5 calls"}
 

@@ -256,7 +256,8 @@ constexpr int kGuMaxSplit = 4;  // most workgroups sharing one item's contractio
 // workgroup b takes part b % KS of it and holds only that part's slice of
 // the operand in LDS, and its partial gate and up sums go to gu_part for the
 // SwiGLU combine.
-// NGL > 0 (bf16, KS = 1): of every KU consecutive units, the last NGL take
+// NGL > 0 (KS = 1; bf16, or fp8 with one column tile): of every KU
+// consecutive units, the last NGL take
 // their operand from global memory (where it stays L2-resident: every
 // workgroup reads the same few hundred KB) and only the others are staged in
 // LDS, so a contraction whose whole operand does not fit in LDS still runs in
@@ -267,7 +268,7 @@ template <int WT, int NT, bool SPLIT, bool FUSED, bool BLDS, int KS, int NGL>
 __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     using C = UnitCfg<WT, NT>;
     constexpr int KU = C::KU;
-    static_assert(NGL == 0 || (WT == 0 && KS == 1 && BLDS && NGL < KU), "mixed operand: bf16, one part, LDS");
+    static_assert(NGL == 0 || (KS == 1 && BLDS && NGL < KU), "mixed operand: one part, LDS, a batch of 2+ units");
     constexpr int KL = KU - NGL;  // units of every KU whose operand is staged in LDS
     using B = Batch<WT, NT, KU>;
     extern __shared__ __align__(16) unsigned char dyn_lds[];
@@ -1006,9 +1007,8 @@ GuPlan plan_gateup(const VerifyParams &p) {
     };
     GuPlan pl{};
     if (try_plan(1, 0, pl)) return pl;
-    if (p.wdtype == 1)
-        for (int ngl = 1; ngl < ku && ngl <= 2; ++ngl)
-            if (try_plan(1, ngl, pl)) return pl;
+    for (int ngl = 1; ngl < ku && ngl <= 2; ++ngl)
+        if (try_plan(1, ngl, pl)) return pl;
     for (int ks = 2; ks <= kGuMaxSplit; ks *= 2) {
         if (nunits % ks != 0) break;
         if (try_plan(ks, 0, pl)) return pl;
@@ -1033,7 +1033,7 @@ hipError_t launch_one(const VerifyParams &p, int n_cu, hipStream_t s, KernelEven
         VerifyParams q = p;
         q.gu_async_x = pl.async_x ? 1 : 0;
         if (pl.fused && pl.blds) {
-            if constexpr (WT == 0) {
+            if constexpr (UnitCfg<WT, NT>::KU > 1) {
                 if (pl.ks == 1 && pl.ngl == 1)
                     return launch_gu(gateup_kernel<WT, NT, SPLIT, true, true, 1, 1>, q, pl.dyn, n_cu, s, ev);
                 if constexpr (UnitCfg<WT, NT>::KU > 2)
