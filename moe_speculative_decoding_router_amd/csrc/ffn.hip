@@ -230,8 +230,11 @@ __device__ __forceinline__ void reduce_waves(f32x4 (&acc)[NT], f32x4 (*red)[NT][
 // measured against 2, 6 and 8 at H = 2880 and 4096; with two column tiles:
 // 8, against 4 at H = 4096 and 20 tokens, 238.5 -> 235.0 us per batched
 // Qwen3 gate-up, where the operand of 2 units in 8 then comes from L2).
+// fp8 (2 KB units): 2 up to two column tiles (at H = 7168 and 20-32 tokens
+// 13-16% faster than 1, which it also lets take the operand partly from
+// L2); with three or four column tiles 2 would spill registers.
 constexpr int gu_batch_units(int wdtype, int nt) {
-    return wdtype == 2 ? (nt == 1 ? 2 : 1) : (nt == 1 ? 4 : (nt == 2 ? 8 : 2));
+    return wdtype == 2 ? (nt <= 2 ? 2 : 1) : (nt == 1 ? 4 : (nt == 2 ? 8 : 2));
 }
 
 template <int WT, int NT>

@@ -248,12 +248,13 @@ def test_bf16_operand_partly_from_l2(H, T):
     verify_workload(wl)
 
 
-@pytest.mark.parametrize("H,T", [(7168, 6), (7168, 8), (7168, 12), (7168, 16), (7040, 8)])
+@pytest.mark.parametrize("H,T", [(7168, 6), (7168, 8), (7168, 12), (7168, 16), (7040, 8), (7168, 20), (7040, 24)])
 def test_fp8_operand_partly_from_l2(H, T):
     """fp8 with the DeepSeek hidden size past the 5 tokens whose operand fits
     in LDS: whole items per workgroup, the operand of one unit in two
-    (2-unit batches of 128-wide blocks) read from L2; H = 7040 has 55
-    blocks, so the last batch of every item is partial."""
+    (2-unit batches of 128-wide blocks) read from L2, with one column tile
+    (T <= 16) and with two (T = 20, 24); H = 7040 has 55 blocks, so the last
+    batch of every item is partial."""
     log(f"case fp8 H={H} T={T} operand partly from L2")
     wl = small("deepseek_fp8", H=H, I=256, E=16, k=4, T=T, shared=True, cid=18)
     verify_workload(wl)
