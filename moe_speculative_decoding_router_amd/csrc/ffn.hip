@@ -331,6 +331,16 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
             if (i0 + lane < c1) load_lds16(xpart + (size_t)src_chunk(i0 + lane) * 8, xs + i0);
     };
 
+    // y starts at zero for the down kernel's two-piece row groups, which it
+    // adds into y.  Zeroed here, at the end of each workgroup's stream (the
+    // stores then delay nothing that waits for memory), rather than by the
+    // router kernel: x, which that kernel reads, may share memory with y.
+    auto zero_y = [&]() {
+        for (int i = (int)blockIdx.x * (kGuWaves * 64) + (int)threadIdx.x; i < T * H;
+             i += (int)gridDim.x * (kGuWaves * 64))
+            p.y[i] = 0.f;
+    };
+
     int nslots;
     if (FUSED) {
         // The chunks that do not overlap the routing scratch are issued by
@@ -368,7 +378,10 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
     wait_vm_all();
     __syncthreads();
     const int items = nslots * rtiles;
-    if ((int)blockIdx.x / KS >= min(items, (int)gridDim.x / KS)) return;
+    if ((int)blockIdx.x / KS >= min(items, (int)gridDim.x / KS)) {
+        zero_y();
+        return;
+    }
 
     // Batches of KU consecutive units; batch b of an item belongs to wave
     // b % kGuWaves, so the workgroup reads one contiguous window that moves
@@ -558,6 +571,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
         if (v1 && (f + 1) % nb == nb - 1) finish_item(acc, f + 1);
         if (!v2) break;
     }
+    zero_y();
 }
 
 // ---------------------------------------------------------------------------
@@ -570,11 +584,16 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
 // row-group segment the waves take interleaved batches, accumulate y for all
 // tokens in registers (the gate weights are already folded into the hidden
 // activations) and meet in LDS in a fixed order.  A workgroup that owns a
-// whole row group writes it to y; the pieces of a row group shared by
-// several workgroups go to the workspace with device-scope stores, and the
-// workgroup that completes the group's piece count adds the pieces in
-// workgroup order (device-scope loads) and writes y.  The result does not
-// depend on timing, and no workgroup waits for another.
+// whole row group writes it to y.  A row group shared by exactly two
+// workgroups (every group when the grid is twice the group count) is added
+// into y, which the gate-up kernel zeroed, by one float atomic add per
+// element from each: 0 + a + b rounds the same in either order, so no
+// count, no wait and no re-read.  With three or more pieces, the pieces go
+// to the workspace with device-scope stores, and the workgroup that
+// completes the group's piece count adds them in workgroup order
+// (device-scope loads) and writes y; starting from 0 it rounds exactly as
+// the two-piece sum.  The result does not depend on timing, and no
+// workgroup waits for another.
 // ---------------------------------------------------------------------------
 constexpr int kDnWaves = 8;
 
@@ -767,6 +786,14 @@ __global__ __launch_bounds__(kDnWaves * 64) void down_kernel(VerifyParams p) {
         __syncthreads();
         const bool whole = qa == 0 && qb == per_group;
         const int first = whole ? 0 : unit_owner(tb, W, G), last = whole ? 0 : unit_owner(te - 1, W, G);
+        // pieces = workgroups in [first, last] with a non-empty range; a row
+        // group of exactly two pieces is added into y (zeroed by the router
+        // kernel) by two float atomic adds: 0 + a + b rounds the same in
+        // either order, and the same as the fix-up's sum
+        int np = 0;
+        for (int ob = first; !whole && ob <= last; ++ob)
+            np += (long long)ob * W / G < (long long)(ob + 1) * W / G ? 1 : 0;
+        const bool pair = !whole && np == 2;
         if (w == 0) {
 #pragma unroll
             for (int q2 = 1; q2 < kDnWaves; ++q2)
@@ -790,6 +817,12 @@ __global__ __launch_bounds__(kDnWaves * 64) void down_kernel(VerifyParams p) {
                         if (rt < rtiles)
                             *reinterpret_cast<float4 *>(p.y + (size_t)t * H + 16 * rt + 4 * g) =
                                 make_float4(v[n][0], v[n][1], v[n][2], v[n][3]);
+                    } else if (pair) {
+                        if (rt < rtiles)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                __hip_atomic_fetch_add(p.y + (size_t)t * H + 16 * rt + 4 * g + j, v[n][j],
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     } else {
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
@@ -798,21 +831,17 @@ __global__ __launch_bounds__(kDnWaves * 64) void down_kernel(VerifyParams p) {
                     }
                 }
             }
-            if (!whole) {
+            if (!whole && !pair) {
                 // once the piece's stores have completed, the group's piece
                 // counter counts it
                 wait_vm_all();
                 if (lane == 0) {
-                    // pieces = workgroups in [first, last] with a non-empty range
-                    int np = 0;
-                    for (int ob = first; ob <= last; ++ob)
-                        np += (long long)ob * W / G < (long long)(ob + 1) * W / G ? 1 : 0;
                     last_sh = __hip_atomic_fetch_add(p.tile_cnt + rg, 1, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT) == np - 1;
                 }
             }
         }
-        if (!whole) {
+        if (!whole && !pair) {
             __syncthreads();
             if (last_sh && w == 0) {
                 // every piece is complete: add them in workgroup order; a
