@@ -133,6 +133,103 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int N, const float 
 }
 
 
+// Small trees (N <= 16 nodes, W <= 64 MW words) in large batches: one wave
+// per tree, four trees per workgroup, the whole tree in registers.  Lane l
+// holds word l + 64 m (m < MW) of every node's footprint and of B, so a
+// round is 16 MW and-not-popcounts per lane, a fold of the 16 counts across
+// the wave that leaves lane i with the count of node i % 16, one score per
+// lane and a wave arg-max: no LDS and no barrier.
+// The scores, their order and the tie rule are those of select_kernel.
+// Against it at 4096 trees of 14 nodes: 54.0 -> 24.4 us (376 words),
+// 35.3 -> 18.0 (144), 59.0 -> 29.2 (464); with one wave sum per node instead
+// of the fold, 32.9 / 23.5 / 37.9.  A single tree takes longer in one wave
+// (11.5 against 8.2 us at 144 words), so small batches keep select_kernel.
+constexpr int kSelWaveNodes = 16;
+constexpr int kSelWaveMinTrees = 512;  // batches from which one wave per tree pays
+
+template <int MW>
+__global__ __launch_bounds__(256) void select_wave_kernel(int N, const float *__restrict__ P,
+                                                          const uint32_t *__restrict__ F, int W, int gamma,
+                                                          float eps, int nt, int update_b, int32_t *S) {
+    constexpr int NM = kSelWaveNodes;
+    const int lane = threadIdx.x & 63;
+    const int tree = (int)blockIdx.x * 4 + ((int)threadIdx.x >> 6);
+    if (tree >= nt) return;  // whole waves only; nothing below synchronises
+    const uint32_t *Ft = F + (size_t)tree * N * W;
+    uint32_t f[NM][MW], b[MW];
+    float pn[NM];
+#pragma unroll
+    for (int n = 0; n < NM; ++n) {
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+            const int i = lane + 64 * m;
+            f[n][m] = (n < N && i < W) ? __builtin_nontemporal_load(Ft + (size_t)n * W + i) : 0u;
+        }
+        pn[n] = n < N ? P[(size_t)tree * N + n] : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < MW; ++m) b[m] = 0u;
+    uint32_t chosen = 0u;
+    for (int r = 0; r < gamma; ++r) {
+        // every node's count, with no branch between them so that the 16
+        // wave sums interleave
+        int c[NM];
+#pragma unroll
+        for (int n = 0; n < NM; ++n) {
+            int x = 0;
+#pragma unroll
+            for (int m = 0; m < MW; ++m) x += __popc(f[n][m] & ~b[m]);
+            c[n] = x;
+        }
+        // fold the 16 counts inside each row of 16 lanes, halving the counts
+        // a lane keeps at every step (partners: mirror in the row, bit 3;
+        // mirror in the half row, bit 2; quad xor 2, bit 1; quad xor 1,
+        // bit 0), so lane i ends with its row's sum for node i % 16; then
+        // add the four rows.  Lane i scores node i % 16 (one division per
+        // lane), and one wave arg-max picks the best.
+        const int me = lane & (NM - 1);
+        const bool h3 = (lane >> 3) & 1, h2 = (lane >> 2) & 1, h1 = (lane >> 1) & 1, h0 = lane & 1;
+        int c8[8], c4[4], c2[2];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            c8[k] = (h3 ? c[k + 8] : c[k]) + __builtin_amdgcn_update_dpp(0, h3 ? c[k] : c[k + 8], 0x140, 0xF, 0xF, false);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            c4[k] = (h2 ? c8[k + 4] : c8[k]) + __builtin_amdgcn_update_dpp(0, h2 ? c8[k] : c8[k + 4], 0x141, 0xF, 0xF, false);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            c2[k] = (h1 ? c4[k + 2] : c4[k]) + __builtin_amdgcn_update_dpp(0, h1 ? c4[k] : c4[k + 2], 0x4E, 0xF, 0xF, false);
+        int cme = (h0 ? c2[1] : c2[0]) + __builtin_amdgcn_update_dpp(0, h0 ? c2[0] : c2[1], 0xB1, 0xF, 0xF, false);
+        cme += __shfl_xor(cme, 16);
+        cme += __shfl_xor(cme, 32);
+        float pme = 0.f;
+#pragma unroll
+        for (int n = 0; n < NM; ++n) pme = me == n ? pn[n] : pme;
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+        if (me < N && !((chosen >> me) & 1u)) {
+            const float v = __fdiv_rn(pme, __fadd_rn((float)cme, eps));
+            bv = v != v ? -INFINITY : v;
+            bi = me;
+        }
+        wave_argmax(bv, bi);
+        bi = __builtin_amdgcn_readfirstlane(bi);
+        if (bi < 0 || bi >= N) {  // unreachable for gamma <= N; kept memory-safe
+            bi = 0;
+            while (bi < N - 1 && ((chosen >> bi) & 1u)) ++bi;
+        }
+        if (lane == 0) S[(size_t)tree * gamma + r] = bi;
+        chosen |= 1u << bi;
+        if (update_b) {
+#pragma unroll
+            for (int n = 0; n < NM; ++n)
+                if (n == bi)
+#pragma unroll
+                    for (int m = 0; m < MW; ++m) b[m] |= f[n][m];
+        }
+    }
+}
+
 // One workgroup (256 threads) per tree.  Every round, groups of TPN threads
 // count the new pairs popcount(F & ~B) of all nodes outside S in parallel;
 // wave 0 then takes, in generation order from the scan position, the first
@@ -263,6 +360,18 @@ size_t select_lds_bytes(int N, int W, bool staged) {
 
 hipError_t launch_select(int N, const float *P, const uint32_t *F, int W, int gamma, float eps, int nt,
                          int32_t *S, bool update_b, hipStream_t s) {
+    if (N <= kSelWaveNodes && W <= 8 * 64 && nt >= kSelWaveMinTrees) {
+        const dim3 g((nt + 3) / 4), b(256);
+        const int ub = update_b ? 1 : 0;
+        const int mw = (W + 63) / 64;
+        if (mw <= 1) hipLaunchKernelGGL(select_wave_kernel<1>, g, b, 0, s, N, P, F, W, gamma, eps, nt, ub, S);
+        else if (mw <= 2) hipLaunchKernelGGL(select_wave_kernel<2>, g, b, 0, s, N, P, F, W, gamma, eps, nt, ub, S);
+        else if (mw <= 3) hipLaunchKernelGGL(select_wave_kernel<3>, g, b, 0, s, N, P, F, W, gamma, eps, nt, ub, S);
+        else if (mw <= 4) hipLaunchKernelGGL(select_wave_kernel<4>, g, b, 0, s, N, P, F, W, gamma, eps, nt, ub, S);
+        else if (mw <= 6) hipLaunchKernelGGL(select_wave_kernel<6>, g, b, 0, s, N, P, F, W, gamma, eps, nt, ub, S);
+        else hipLaunchKernelGGL(select_wave_kernel<8>, g, b, 0, s, N, P, F, W, gamma, eps, nt, ub, S);
+        return hipGetLastError();
+    }
     // threads per node: the largest power of two <= min(64, 256 / N), at least 1
     int tpn = 1;
     while (tpn * 2 <= 64 && tpn * 2 * N <= kSelThreads) tpn *= 2;

@@ -25,33 +25,61 @@ def run_select(trees, gamma, eps=1e-6, static=False):
     return S.cpu().numpy()
 
 
+def check_select_tiled(trees, gamma, ref, static=False):
+    """The batch as given (one workgroup per tree below 512 trees) and tiled
+    8 times (one wave per tree from 512 trees on, for N <= 16 and W <= 512):
+    every tree's selection equals the oracle's."""
+    for reps in (1, 8):
+        P = np.ascontiguousarray(np.tile(trees.P, (reps, 1)))
+        F = np.ascontiguousarray(np.tile(trees.F, (reps, 1, 1)))
+        S = m.select_drafts(trees.parent, to_dev(P), to_dev(F.view(np.int32)), gamma, 1e-6, static=static)
+        torch.cuda.synchronize()
+        assert np.array_equal(S.cpu().numpy(), np.tile(ref, (reps, 1))), f"batch of {P.shape[0]} trees"
+
+
 @pytest.mark.parametrize("gamma", [0, 1, 4, 14])
 def test_select_gptoss_trees(gamma):
-    log(f"case select_drafts gptoss trees nt=128 gamma={gamma}")
+    log(f"case select_drafts gptoss trees nt=128 (and 1024) gamma={gamma}")
     trees = synth.draft_trees(seed=0, nt=128, n_layers=36, E=128, k=4)
-    S = run_select(trees, gamma)
-    ref = osel.select_drafts_batch(trees.P, trees.F, gamma)
-    assert np.array_equal(S, ref)
+    check_select_tiled(trees, gamma, osel.select_drafts_batch(trees.P, trees.F, gamma))
 
 
 @pytest.mark.parametrize("gamma", [1, 4, 6])
 def test_select_static_cost(gamma):
-    log(f"case select_drafts_static gptoss trees nt=128 gamma={gamma}")
+    log(f"case select_drafts_static gptoss trees nt=128 (and 1024) gamma={gamma}")
     trees = synth.draft_trees(seed=0, nt=128, n_layers=36, E=128, k=4)
-    S = run_select(trees, gamma, static=True)
-    assert np.array_equal(S, osel.select_drafts_batch(trees.P, trees.F, gamma, static=True))
+    check_select_tiled(trees, gamma, osel.select_drafts_batch(trees.P, trees.F, gamma, static=True), static=True)
 
 
 def test_select_ties_and_odd_widths():
-    log("case select_drafts ties / odd W")
+    log("case select_drafts ties / odd W, nt=64 (and 512)")
     trees = synth.draft_trees(seed=1, nt=64, n_layers=5, E=37, k=3)   # W = 6 words
     trees.P[:] = np.float32(0.5)
-    S = run_select(trees, 5)
-    assert np.array_equal(S, osel.select_drafts_batch(trees.P, trees.F, 5))
+    check_select_tiled(trees, 5, osel.select_drafts_batch(trees.P, trees.F, 5))
     trees.F[:] = trees.F[:, :1]                                          # all footprints equal
     trees.P[:] = np.random.default_rng(3).uniform(0.1, 1, trees.P.shape).astype(np.float32)
-    S = run_select(trees, 7)
-    assert np.array_equal(S, osel.select_drafts_batch(trees.P, trees.F, 7))
+    check_select_tiled(trees, 7, osel.select_drafts_batch(trees.P, trees.F, 7))
+
+
+@pytest.mark.parametrize("N,W", [(16, 1), (16, 64), (9, 65), (16, 130), (12, 200), (16, 256), (15, 300), (16, 512),
+                                 (3, 7)])
+def test_select_register_resident_shapes(N, W):
+    """Every register width of the one-wave-per-tree kernel (64, 128, 192,
+    256, 384 and 512 words, partial last blocks, N up to 16) on 64 random
+    trees tiled to 512, marginal and static cost, gamma 4 and N; ties in P."""
+    log(f"case select_drafts register-resident N={N} W={W}")
+    rng = np.random.default_rng(1000 + 7 * N + W)
+    nt = 64
+    F = (rng.random((nt, N, W * 32)) < 0.3)
+    F = np.packbits(F, axis=2, bitorder="little").view(np.uint32).reshape(nt, N, W)
+    P = rng.choice(np.array([0.25, 0.5, 0.75, 1.0], dtype=np.float32), size=(nt, N))
+    parent = np.array([-1] + [(i - 1) // 2 for i in range(1, N)], dtype=np.int32)
+    trees = type("Trees", (), {})()
+    trees.parent, trees.P, trees.F = parent, np.ascontiguousarray(P), np.ascontiguousarray(F)
+    for gamma in sorted({min(4, N), N}):
+        for static in (False, True):
+            check_select_tiled(trees, gamma, osel.select_drafts_batch(trees.P, trees.F, gamma, static=static),
+                               static=static)
 
 
 def test_select_large_batch_sampled():
