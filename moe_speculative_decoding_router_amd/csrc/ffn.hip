@@ -366,7 +366,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void gateup_kernel(VerifyParams p) {
             for (int c = w - T; c < nkt / 2; c += kGuWaves - T) load_lds16(sht + (size_t)c * 1024, &red[0][w][0][0]);
         }
         // routing, recomputed by every workgroup (bit-identical results)
-        block_route<kGuWaves * 64>(p, scr, sexp, nullptr, fin, &nslots_sh, blockIdx.x == 0, after_pass1);
+        block_route<kGuWaves * 64>(p, scr, sexp, nullptr, fin, &nslots_sh, blockIdx.x == 0, after_pass1,
+                                   (int)gridDim.x);
         nslots = nslots_sh;
         if (early < nx) stage_x(0, kGuWaves, early, nx);
     } else {

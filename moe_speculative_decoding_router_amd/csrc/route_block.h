@@ -296,9 +296,11 @@ struct RouteScratch {
 //        expert and gate weight of rank j of token t.
 //   tw (when not NULL; LDS or global, written only): tw[s * T + t] gate
 //        weight of token t in slot s (0 if not routed).
-//   global (when write_global): topk_idx, topk_w, union, CSR, P* (each
-//        sequence's, ascending), meta, the slot tables (slot_expert, tokw,
-//        tokpos, tpos) of the FFN kernels.
+//   global (when write_global): topk_idx, topk_w, union, CSR row offsets,
+//        P* (each sequence's, ascending), meta, slot_expert; the CSR entries
+//        and the slot tables (tokw, tokpos, tpos) of the FFN kernels when
+//        write_global, or part blockIdx.x of them when tab_parts > 1 (the
+//        tab_parts calling workgroups then write the whole tables together).
 // The first pass gives token t to wave t % (NTHREADS / 64); waves without a
 // token wait at the barrier that ends it (the caller may hand them other work
 // before the call).  Barriers: pass 1, [bias: importance and preferred set
@@ -306,7 +308,8 @@ struct RouteScratch {
 // NJ: row entries per lane the selections scan (>= ceil(E / 64)).
 template <int NTHREADS, int NJ, typename Hook>
 __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned char *scratch, int *sexp, float *tw,
-                                               int *fin, int *nslots_lds, bool write_global, const Hook &after_pass1) {
+                                               int *fin, int *nslots_lds, bool write_global, const Hook &after_pass1,
+                                               int tab_parts) {
     static_assert(NTHREADS >= kMaxExperts, "the union scan gives every expert one thread");
     constexpr int NW = NTHREADS / 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -523,9 +526,19 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
     lds_barrier();
 
     // ---- slot tables and CSR entries: one thread per (slot, token), each
-    //      entry written once ----
+    //      entry written once.  With tab_parts > 1 the calling workgroups
+    //      split the entries: workgroup b computes and writes part b only
+    //      (the gate-up kernel, whose workgroups read each token's final
+    //      selection instead of the tables) ----
     const int U = sh.misc[0];
-    for (int i = tid; i < U * T; i += NTHREADS) {
+    const int nent = U * T;
+    const bool wtab = write_global || tab_parts > 1;
+    int e0 = 0, e1 = (tw != nullptr || write_global) ? nent : 0;
+    if (tab_parts > 1) {
+        e0 = (int)((long long)nent * blockIdx.x / tab_parts);
+        e1 = (int)((long long)nent * (blockIdx.x + 1) / tab_parts);
+    }
+    for (int i = e0 + tid; i < e1; i += NTHREADS) {
         const int r = i / T, t = i - r * T;  // union rank, token
         const int s = r + so;                // slot
         const int e = sexp[s];
@@ -538,14 +551,14 @@ __device__ __forceinline__ void block_route_nj(const VerifyParams &p, unsigned c
                 if (sh.fin_i[t * k + j] == e) jj = j;
             wt = sh.fin_w[t * k + jj];
             pos = slot_off[r] + __popcll(msk & ((1ull << t) - 1ull));
-            if (write_global) {
+            if (wtab) {
                 p.csr_tok[pos] = t;
                 p.csr_w[pos] = wt;
                 p.tpos[t * k + jj] = pos;
             }
         }
         if (tw) tw[s * T + t] = wt;
-        if (write_global) {
+        if (wtab) {
             p.tokw[(size_t)s * T + t] = wt;
             p.tokpos[(size_t)s * T + t] = pos;
         }
@@ -583,13 +596,14 @@ struct NoHook {
 template <int NTHREADS, typename Hook = NoHook>
 __device__ __forceinline__ void block_route(const VerifyParams &p, unsigned char *scratch, int *sexp, float *tw,
                                             int *fin, int *nslots_lds, bool write_global,
-                                            const Hook &after_pass1 = Hook{}) {
+                                            const Hook &after_pass1 = Hook{}, int tab_parts = 1) {
     if (p.E <= 128)
-        block_route_nj<NTHREADS, 2>(p, scratch, sexp, tw, fin, nslots_lds, write_global, after_pass1);
+        block_route_nj<NTHREADS, 2>(p, scratch, sexp, tw, fin, nslots_lds, write_global, after_pass1, tab_parts);
     else if (p.E <= 256)
-        block_route_nj<NTHREADS, 4>(p, scratch, sexp, tw, fin, nslots_lds, write_global, after_pass1);
+        block_route_nj<NTHREADS, 4>(p, scratch, sexp, tw, fin, nslots_lds, write_global, after_pass1, tab_parts);
     else
-        block_route_nj<NTHREADS, kRouteNJ>(p, scratch, sexp, tw, fin, nslots_lds, write_global, after_pass1);
+        block_route_nj<NTHREADS, kRouteNJ>(p, scratch, sexp, tw, fin, nslots_lds, write_global, after_pass1,
+                                           tab_parts);
 }
 
 }  // namespace moe
