@@ -232,9 +232,12 @@ int union_stats(const int32_t *topk_idx, int32_t nL, int32_t T, int32_t k, int32
  * divide, each correctly rounded), choose the highest score (ties: lowest
  * node index), B |= F_chosen.  S [nt, gamma] int32 receives node ids in
  * choice order.  P, Epred and S may be NULL when gamma == 0 or nt == 0.
- * Limits: 0 <= gamma <= N <= 4096, 1 <= W <= 4096, eps > 0.  A tree whose
+ * Limits: 0 <= gamma <= N <= 4096, 1 <= W <= 4096, eps > 0.  Batches of
+ * 512 or more trees with N <= 16 and W <= 512 run one wave per tree with the
+ * tree in registers; otherwise one workgroup per tree, and a tree whose
  * footprints fit in 64 KB of LDS (N * W + W + N + N / 32 <= 16384 words) is
- * staged there once; a larger one is read from global memory every round. */
+ * staged there once, a larger one read from global memory every round.
+ * Every path gives the same selections. */
 int select_drafts(const int32_t *parent, int32_t N, const float *P, const uint32_t *Epred,
                   int32_t W, int32_t gamma, float eps, int32_t nt, int32_t *S, void *stream);
 
