@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(VerifyParams p) 
                 }
             }
             __syncthreads();
-            if (threadIdx.x < nt) {
+            if ((int)threadIdx.x < nt) {
                 const int tt = threadIdx.x;
                 float sum = red[0][tt];
 #pragma unroll

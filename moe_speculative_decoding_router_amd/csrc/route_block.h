@@ -148,7 +148,7 @@ __device__ __forceinline__ unsigned wave_topk_mask(const unsigned (&key)[kRouteN
         const unsigned km = key[j] & M;
         const bool eq = v && km == P;
         const unsigned long long bal = __ballot(eq);
-        const bool s = (v && km > P) || (eq && (!ties || __popcll(bal & below) < left));
+        const bool s = (v && km > P) || (eq && (!ties || (int)__popcll(bal & below) < left));
         left -= __popcll(bal);
         if (s) sel |= 1u << j;
     }
