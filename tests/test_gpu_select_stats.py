@@ -61,6 +61,22 @@ def test_select_ties_and_odd_widths():
     check_select_tiled(trees, 7, osel.select_drafts_batch(trees.P, trees.F, 7))
 
 
+def test_select_register_resident_ragged_batch():
+    """One wave per tree, four trees per workgroup: 515 trees leave the last
+    workgroup with three idle waves; N = 1 and N = 2 trees included."""
+    log("case select_drafts register-resident nt=515, N in {1, 2, 5}")
+    rng = np.random.default_rng(77)
+    for N, W, gamma in ((1, 3, 1), (2, 40, 2), (5, 100, 3)):
+        F = np.packbits(rng.random((515, N, W * 32)) < 0.2, axis=2, bitorder="little").view(np.uint32)
+        F = np.ascontiguousarray(F.reshape(515, N, W))
+        P = np.ascontiguousarray(rng.uniform(0.05, 1.0, (515, N)).astype(np.float32))
+        parent = np.array([-1] + [(i - 1) // 2 for i in range(1, N)], dtype=np.int32)
+        for static in (False, True):
+            S = m.select_drafts(parent, to_dev(P), to_dev(F.view(np.int32)), gamma, 1e-6, static=static)
+            torch.cuda.synchronize()
+            assert np.array_equal(S.cpu().numpy(), osel.select_drafts_batch(P, F, gamma, static=static))
+
+
 @pytest.mark.parametrize("N,W", [(16, 1), (16, 64), (9, 65), (16, 130), (12, 200), (16, 256), (15, 300), (16, 512),
                                  (3, 7)])
 def test_select_register_resident_shapes(N, W):
