@@ -234,6 +234,7 @@ def measure_workload(m, synth, args, name, dev, headline):
         rec["cost_model"] = calibrate_cost_model(m, synth, wl, layers, dev)
     if headline:
         rec["select_4096_trees"] = select_timing(m, synth, wl, dev, stream, nt=4096)
+        rec["expand_4096_trees"] = expand_timing(m, synth, wl, dev, stream, rec.get("cost_model"), nt=4096)
         if wl.n_seq > 1 and not args.no_ab:
             rec["config_ab"] = config_ab(m, synth, wl, layers, dev)
         if args.ablation:
@@ -507,6 +508,49 @@ def config_ab(m, synth, wl, layers, dev, reps=15):
         f"on (per sequence): U {rb['on_per_sequence']['unique_experts_per_layer']}, "
         f"{rb['on_per_sequence']['verify_kernel_us_per_layer']} us")
     return res
+
+
+def expand_timing(m, synth, wl, dev, stream, cost_model, nt=4096, reps=20):
+    """expand_drafts (S2-MoE utility expansion) on a batch of nt draft trees of
+    this workload's shape, one launch for the batch.  The cost model's terms
+    come from the calibration when it ran (T_exp per streamed expert; T_AR =
+    the verify time of one token per layer times the model's layers), else
+    6 us per expert and 60 us per layer; the draft cost is zero."""
+    import numpy as np
+    import torch
+    ML = MODEL_LAYERS[wl.name]
+    t_exp, t_layer = 6.0, 60.0
+    if cost_model:
+        t_exp = float(cost_model["t_exp_us_per_unique_expert"])
+        t_layer = float(cost_model["per_T_experts_us"][0][2])
+    t_ar = ML * t_layer
+    base = min(nt, 256)
+    trees = synth.draft_trees(seed=5, nt=base, n_layers=ML, E=wl.E, k=wl.k)
+    reps_t = (nt + base - 1) // base
+    P_d = torch.from_numpy(np.ascontiguousarray(np.tile(trees.P, (reps_t, 1))[:nt])).to(dev)
+    F = np.ascontiguousarray(np.tile(trees.F, (reps_t, 1, 1))[:nt])
+    F_d = torch.from_numpy(F.view(np.int32)).to(dev)
+    for _ in range(3):
+        S, cnt = m.expand_drafts(trees.parent, P_d, F_d, t_ar, t_exp)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pad = torch.empty(1 << 28, dtype=torch.uint8, device=dev)  # queue ahead, as in select_timing
+    for _ in range(40):
+        pad.fill_(1)
+    a.record(stream)
+    for _ in range(reps):
+        S, cnt = m.expand_drafts(trees.parent, P_d, F_d, t_ar, t_exp)
+    b.record(stream)
+    torch.cuda.synchronize()
+    del pad
+    us = a.elapsed_time(b) / reps * 1e3
+    nbytes = F.nbytes + nt * F.shape[1] * 4
+    joined = float(cnt.float().mean())
+    err(f"[bench] expand_drafts, {nt} trees: {us:.1f} us per launch, {nbytes / (us * 1e-6) / 1e9:.0f} GB/s, "
+        f"{joined:.2f} nodes joined per tree")
+    return {"trees": nt, "distinct_trees": base, "nodes_per_tree": int(F.shape[1]), "words_per_footprint": int(F.shape[2]),
+            "t_ar_us": round(t_ar, 1), "t_exp_us": round(t_exp, 3), "nodes_joined_per_tree": round(joined, 3),
+            "us_per_launch": round(us, 2), "bytes_read": int(nbytes), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def select_timing(m, synth, wl, dev, stream, nt=4096, reps=20):

@@ -133,6 +133,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(int N, const float 
 }
 
 
+// The 16 node counts of a one-wave-per-tree kernel (c[n]: this lane's part
+// of node n's count) folded across the wave, halving the counts a lane keeps
+// at every step: partners are the mirror lane in the row (lane bit 3), in
+// the half row (bit 2), then quad xor 2 (bit 1) and xor 1 (bit 0), so lane
+// i ends with its row's sum for node i % 16; the four rows are then added.
+// Integer sums, exact in any order.
+__device__ __forceinline__ int fold_node_counts(const int (&c)[16]) {
+    const int lane = threadIdx.x & 63;
+    const bool h3 = (lane >> 3) & 1, h2 = (lane >> 2) & 1, h1 = (lane >> 1) & 1, h0 = lane & 1;
+    int c8[8], c4[4], c2[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        c8[k] = (h3 ? c[k + 8] : c[k]) + __builtin_amdgcn_update_dpp(0, h3 ? c[k] : c[k + 8], 0x140, 0xF, 0xF, false);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        c4[k] = (h2 ? c8[k + 4] : c8[k]) + __builtin_amdgcn_update_dpp(0, h2 ? c8[k] : c8[k + 4], 0x141, 0xF, 0xF, false);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        c2[k] = (h1 ? c4[k + 2] : c4[k]) + __builtin_amdgcn_update_dpp(0, h1 ? c4[k] : c4[k + 2], 0x4E, 0xF, 0xF, false);
+    int cnt = (h0 ? c2[1] : c2[0]) + __builtin_amdgcn_update_dpp(0, h0 ? c2[0] : c2[1], 0xB1, 0xF, 0xF, false);
+    cnt += __shfl_xor(cnt, 16);
+    cnt += __shfl_xor(cnt, 32);
+    return cnt;
+}
+
 // Small trees (N <= 16 nodes, W <= 64 MW words) in large batches: one wave
 // per tree, four trees per workgroup, the whole tree in registers.  Lane l
 // holds word l + 64 m (m < MW) of every node's footprint and of B, so a
@@ -181,27 +206,10 @@ __global__ __launch_bounds__(256) void select_wave_kernel(int N, const float *__
             for (int m = 0; m < MW; ++m) x += __popc(f[n][m] & ~b[m]);
             c[n] = x;
         }
-        // fold the 16 counts inside each row of 16 lanes, halving the counts
-        // a lane keeps at every step (partners: mirror in the row, bit 3;
-        // mirror in the half row, bit 2; quad xor 2, bit 1; quad xor 1,
-        // bit 0), so lane i ends with its row's sum for node i % 16; then
-        // add the four rows.  Lane i scores node i % 16 (one division per
-        // lane), and one wave arg-max picks the best.
+        // lane i scores node i % 16 (one division per lane), and one wave
+        // arg-max picks the best
         const int me = lane & (NM - 1);
-        const bool h3 = (lane >> 3) & 1, h2 = (lane >> 2) & 1, h1 = (lane >> 1) & 1, h0 = lane & 1;
-        int c8[8], c4[4], c2[2];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            c8[k] = (h3 ? c[k + 8] : c[k]) + __builtin_amdgcn_update_dpp(0, h3 ? c[k] : c[k + 8], 0x140, 0xF, 0xF, false);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            c4[k] = (h2 ? c8[k + 4] : c8[k]) + __builtin_amdgcn_update_dpp(0, h2 ? c8[k] : c8[k + 4], 0x141, 0xF, 0xF, false);
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-            c2[k] = (h1 ? c4[k + 2] : c4[k]) + __builtin_amdgcn_update_dpp(0, h1 ? c4[k] : c4[k + 2], 0x4E, 0xF, 0xF, false);
-        int cme = (h0 ? c2[1] : c2[0]) + __builtin_amdgcn_update_dpp(0, h0 ? c2[0] : c2[1], 0xB1, 0xF, 0xF, false);
-        cme += __shfl_xor(cme, 16);
-        cme += __shfl_xor(cme, 32);
+        const int cme = fold_node_counts(c);
         float pme = 0.f;
 #pragma unroll
         for (int n = 0; n < NM; ++n) pme = me == n ? pn[n] : pme;
@@ -228,6 +236,82 @@ __global__ __launch_bounds__(256) void select_wave_kernel(int N, const float *__
                     for (int m = 0; m < MW; ++m) b[m] |= f[n][m];
         }
     }
+}
+
+// Utility expansion of small trees in large batches, laid out as in
+// select_wave_kernel: one wave per tree, the tree in registers, the node
+// counts folded so that lane i holds node i % 16's.  Every round each lane
+// tests its node (outside S, its parent in S or the root, at or after the
+// scan position, utility test passed) and the lowest passing node joins;
+// the passes, the float32 test and the order are those of expand_kernel.
+template <int MW>
+__global__ __launch_bounds__(256) void expand_wave_kernel(ExpandArgs a, const float *__restrict__ P,
+                                                          const uint32_t *__restrict__ F,
+                                                          const float *__restrict__ Cd, int32_t *S, int32_t *count) {
+    constexpr int NM = kSelWaveNodes;
+    const int lane = threadIdx.x & 63;
+    const int tree = (int)blockIdx.x * 4 + ((int)threadIdx.x >> 6);
+    if (tree >= a.nt) return;  // whole waves only; nothing below synchronises
+    const int N = a.N, W = a.W;
+    const uint32_t *Ft = F + (size_t)tree * N * W;
+    uint32_t f[NM][MW], b[MW];
+#pragma unroll
+    for (int n = 0; n < NM; ++n)
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+            const int i = lane + 64 * m;
+            f[n][m] = (n < N && i < W) ? __builtin_nontemporal_load(Ft + (size_t)n * W + i) : 0u;
+        }
+    const int me = lane & (NM - 1);
+    const float pme = me < N ? P[(size_t)tree * N + me] : 0.f;
+    const float cdme = (me < N && Cd) ? Cd[(size_t)tree * N + me] : 0.f;
+    int par = -1;  // parent of node me (static indices into the argument block)
+#pragma unroll
+    for (int n = 0; n < NM; ++n)
+        if (me == n && n < N) par = a.parent[n];
+#pragma unroll
+    for (int m = 0; m < MW; ++m) b[m] = 0u;
+    uint32_t inS = 0u;
+    int pos = 0, nsel = 0;
+    bool added = false;
+    for (int round = 0; round <= 2 * N; ++round) {
+        int c[NM];
+#pragma unroll
+        for (int n = 0; n < NM; ++n) {
+            int x = 0;
+#pragma unroll
+            for (int m = 0; m < MW; ++m) x += __popc(f[n][m] & ~b[m]);
+            c[n] = x;
+        }
+        const int cme = fold_node_counts(c);
+        bool ok = false;
+        if (me < N && me >= pos && !((inS >> me) & 1u) && (par < 0 || ((inS >> par) & 1u))) {
+            const float num = __fmul_rn(pme, a.t_ar);
+            const float den = __fadd_rn(__fmul_rn((float)cme, a.t_exp), cdme);
+            ok = num >= den;
+        }
+        const unsigned long long bal = __ballot(ok) & 0xFFFFull;  // lanes 0..15 hold nodes 0..15
+        const int pick = bal ? (int)__builtin_ctzll(bal) : -1;
+        if (pick >= 0) {
+            inS |= 1u << pick;
+            if (lane == 0) S[(size_t)tree * N + nsel] = pick;
+#pragma unroll
+            for (int n = 0; n < NM; ++n)
+                if (n == pick)
+#pragma unroll
+                    for (int m = 0; m < MW; ++m) b[m] |= f[n][m];
+            pos = pick + 1;
+            added = true;
+            ++nsel;
+        } else if (added) {  // a new pass from node 0
+            pos = 0;
+            added = false;
+        } else {
+            break;
+        }
+    }
+    for (int i = nsel + lane; i < N; i += 64) S[(size_t)tree * N + i] = -1;
+    if (lane == 0) count[tree] = nsel;
 }
 
 // One workgroup (256 threads) per tree.  Every round, groups of TPN threads
@@ -341,6 +425,17 @@ size_t expand_lds_bytes(int N, int W, bool staged) {
 
 hipError_t launch_expand(ExpandArgs a, const float *P, const uint32_t *F, const float *Cd, int32_t *S,
                          int32_t *count, hipStream_t s) {
+    if (a.N <= kSelWaveNodes && a.W <= 8 * 64 && a.nt >= kSelWaveMinTrees) {
+        const dim3 g((a.nt + 3) / 4), b(256);
+        const int mw = (a.W + 63) / 64;
+        if (mw <= 1) hipLaunchKernelGGL(expand_wave_kernel<1>, g, b, 0, s, a, P, F, Cd, S, count);
+        else if (mw <= 2) hipLaunchKernelGGL(expand_wave_kernel<2>, g, b, 0, s, a, P, F, Cd, S, count);
+        else if (mw <= 3) hipLaunchKernelGGL(expand_wave_kernel<3>, g, b, 0, s, a, P, F, Cd, S, count);
+        else if (mw <= 4) hipLaunchKernelGGL(expand_wave_kernel<4>, g, b, 0, s, a, P, F, Cd, S, count);
+        else if (mw <= 6) hipLaunchKernelGGL(expand_wave_kernel<6>, g, b, 0, s, a, P, F, Cd, S, count);
+        else hipLaunchKernelGGL(expand_wave_kernel<8>, g, b, 0, s, a, P, F, Cd, S, count);
+        return hipGetLastError();
+    }
     int tpn = 1;
     while (tpn * 2 <= 64 && tpn * 2 * a.N <= kSelThreads) tpn *= 2;
     a.tpn = tpn;

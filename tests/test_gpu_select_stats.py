@@ -121,13 +121,42 @@ def test_expand_gptoss_trees(t_ar, t_exp, with_cd):
     trees = synth.draft_trees(seed=4, nt=256, n_layers=36, E=128, k=4)
     cd = (np.random.default_rng(9).uniform(0, 20, trees.P.shape).astype(np.float32) if with_cd
           else np.zeros(trees.P.shape, np.float32))
-    S, cnt = m.expand_drafts(trees.parent, to_dev(trees.P), to_dev(trees.F.view(np.int32)), t_ar, t_exp,
-                             to_dev(cd) if with_cd else None)
-    torch.cuda.synchronize()
     ref = oexp.expand_batch(trees.parent, trees.P, trees.F, t_ar, t_exp, cd)
+    # as given (one workgroup per tree) and tiled to 512 trees (one wave per tree)
+    for reps in (1, 2):
+        P = np.ascontiguousarray(np.tile(trees.P, (reps, 1)))
+        F = np.ascontiguousarray(np.tile(trees.F, (reps, 1, 1)))
+        C = np.ascontiguousarray(np.tile(cd, (reps, 1)))
+        S, cnt = m.expand_drafts(trees.parent, to_dev(P), to_dev(F.view(np.int32)), t_ar, t_exp,
+                                 to_dev(C) if with_cd else None)
+        torch.cuda.synchronize()
+        assert np.array_equal(S.cpu().numpy(), np.tile(ref, (reps, 1))), f"batch of {P.shape[0]} trees"
+        assert np.array_equal(cnt.cpu().numpy(), np.tile((ref >= 0).sum(axis=1), reps))
+    log(f"    nodes per tree: mean {float((ref >= 0).sum(axis=1).mean()):.2f}")
+
+
+@pytest.mark.parametrize("N,W", [(16, 1), (16, 64), (9, 65), (12, 200), (16, 256), (15, 300), (16, 512), (1, 5)])
+def test_expand_register_resident_shapes(N, W):
+    """Every register width of the one-wave-per-tree expansion on random
+    BFS trees (515 trees: the last workgroup is partly idle), draft costs,
+    and costs that let some but not all nodes join, over several passes."""
+    log(f"case expand_drafts register-resident N={N} W={W}")
+    rng = np.random.default_rng(3000 + 11 * N + W)
+    nt = 515
+    F = np.packbits(rng.random((nt, N, W * 32)) < 0.05, axis=2, bitorder="little").view(np.uint32)
+    F = np.ascontiguousarray(F.reshape(nt, N, W))
+    P = np.ascontiguousarray(rng.uniform(0.05, 1.0, (nt, N)).astype(np.float32))
+    cd = np.ascontiguousarray(rng.uniform(0, 2, (nt, N)).astype(np.float32))
+    parent = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, N)], dtype=np.int32)
+    t_exp = 1.0
+    t_ar = float(np.median(np.unpackbits(F.view(np.uint8), axis=2).sum(axis=2)) * 1.5 + 2)
+    S, cnt = m.expand_drafts(parent, to_dev(P), to_dev(F.view(np.int32)), t_ar, t_exp, to_dev(cd))
+    torch.cuda.synchronize()
+    ref = oexp.expand_batch(parent, P, F, t_ar, t_exp, cd)
     assert np.array_equal(S.cpu().numpy(), ref)
     assert np.array_equal(cnt.cpu().numpy(), (ref >= 0).sum(axis=1))
-    log(f"    nodes per tree: mean {float((ref >= 0).sum(axis=1).mean()):.2f}")
+    joined = (ref >= 0).sum(axis=1)
+    log(f"    nodes per tree: mean {float(joined.mean()):.2f}, max {int(joined.max())}")
 
 
 def test_expand_odd_shapes():
