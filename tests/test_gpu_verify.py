@@ -274,6 +274,23 @@ def test_bf16_gptoss_contraction_tail():
     verify_workload(wl)
 
 
+def test_down_two_and_three_piece_row_groups():
+    """bf16 at H = 2112 (132 row groups): no grid of 224-256 workgroups keeps
+    every row group to two pieces, so 256 workgroups leave 12 groups with two
+    pieces (added into y by the atomics) and 120 with three (the counted
+    fix-up) in the same call; the output matches the oracle and two runs
+    give identical bits."""
+    log("case bf16 H=2112 T=5 (two- and three-piece down row groups)")
+    wl = small("qwen3_bf16", H=2112, I=256, E=16, k=4, T=5, rate=0.05, cid=19)
+    verify_workload(wl)
+    x, _, Wr = synth.layer_inputs(wl, 0)
+    from gpu_helpers import device_layer
+    lw = device_layer(wl, 0, Wr)
+    a = run_layer(lw, x)
+    b = run_layer(lw, x)
+    assert np.array_equal(a["y"], b["y"])
+
+
 @pytest.mark.parametrize("case", ["fp8_straddle", "bf16_multi_group"])
 def test_down_shared_row_groups(case):
     """Down kernel with row groups shared between workgroups.  fp8 at
