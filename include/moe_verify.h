@@ -186,6 +186,8 @@ size_t moe_verify_workspace_bytes(const moe_layer *layer, int32_t T, const moe_b
  * layer (host), bias (host, NULL = off), aux (host, NULL = no extra outputs).
  * ws: device workspace of at least moe_verify_workspace_bytes() bytes,
  * 256-byte aligned; its contents need no initialisation and are clobbered.
+ * y may be x itself (x is read before y is first written); it must not
+ * overlap the workspace, the aux outputs or the weights.
  * Limits: 1 <= T <= 64, 1 <= k <= min(E, 32), E <= 512; bf16: H a multiple of
  * 64 and I of 32; fp8: H, I multiples of 128.  Numerics: router GEMV and FFN
  * accumulate in float32; activations enter the bf16/fp8 matrix-core

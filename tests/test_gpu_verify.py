@@ -274,6 +274,31 @@ def test_bf16_gptoss_contraction_tail():
     verify_workload(wl)
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "f32"])
+def test_output_over_the_input(kind):
+    """y may share memory with x: x is consumed by the router kernel (the
+    float32 path: by its gate-up) before y is cleared or written, so the
+    call with out = x gives the same bits as with a separate output."""
+    import torch
+    log(f"case {kind} output over the input")
+    if kind == "f32":
+        wl = synth.WORKLOADS["tiny_f32"]
+        x, Wr, Wgu, Wd = synth.tiny_f32_arrays(wl)
+        lw = f32_layer(Wr, Wgu, Wd, wl.k)
+    else:
+        wl = small("deepseek_fp8" if kind == "fp8" else "qwen3_bf16", H=2816 if kind == "fp8" else 2112, I=256,
+                   E=16, k=4, T=5, shared=kind == "fp8", rate=0.05, cid=20)
+        x, _, Wr = synth.layer_inputs(wl, 0)
+        from gpu_helpers import device_layer
+        lw = device_layer(wl, 0, Wr)
+    ref, _ = m.verify_layer(to_dev(x), lw)
+    xy = to_dev(x)
+    y, _ = m.verify_layer(xy, lw, out=xy)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == xy.data_ptr()
+    assert np.array_equal(y.cpu().numpy(), ref.cpu().numpy())
+
+
 def test_down_two_and_three_piece_row_groups():
     """bf16 at H = 2112 (132 row groups): no grid of 224-256 workgroups keeps
     every row group to two pieces, so 256 workgroups leave 12 groups with two
